@@ -1,0 +1,193 @@
+"""Python binding of libzs, the MI355X GIE zonal-scatter library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libzs.so`` (C ABI in ``include/zs.h``).  PyTorch supplies device
+memory and the current HIP stream.  There is no CPU fallback: if the library
+is missing or no GPU is present, these functions raise.
+
+Functions carry the C ABI's names:
+
+* ``zs_build_csr(dst, n_nodes)`` -> ``Csr(rowptr, perm, dst32)``
+* ``zs_forward(coupling, radial, csr)`` -> out (N, 16, C)
+* ``zs_backward(grad_out, coupling, radial, csr)`` -> (grad_coupling, grad_radial)
+
+plus ``gie_zonal_scatter(coupling, radial, csr)``, an autograd function with
+the operator boundary of deepmd-kit PR #6072 ("fused Triton zonal scatter for
+the GIE head", section "Boundary and layout contract"): inputs are made
+contiguous first, only fp32 is accepted, and no double backward is provided.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import NamedTuple
+
+import torch  # load torch's HIP runtime first so libzs binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzs.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "zs.h")
+
+ZS_OK = 0
+ROWS, ZONAL, SLOTS = 16, 15, 3
+MAX_CHANNELS = 1024
+
+_lib = None
+
+
+class ZsError(RuntimeError):
+    """A libzs call returned a negative status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libzs.so (built by edge_node_scatter_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I64, SZ, INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+        lib.zs_status_string.argtypes = [INT]
+        lib.zs_status_string.restype = ctypes.c_char_p
+        lib.zs_csr_workspace_bytes.argtypes = [I64, I64]
+        lib.zs_csr_workspace_bytes.restype = SZ
+        lib.zs_build_csr.argtypes = [P, I64, I64, P, P, P, P, SZ, P, P]
+        lib.zs_build_csr.restype = INT
+        lib.zs_forward.argtypes = [P, P, P, P, I64, I64, I64, P, P]
+        lib.zs_forward.restype = INT
+        lib.zs_backward.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, P, P]
+        lib.zs_backward.restype = INT
+        _lib = lib
+    return _lib
+
+
+def declared_symbols() -> list[str]:
+    """Function names declared in include/zs.h."""
+    text = open(HEADER_PATH).read()
+    return re.findall(r"^\w[\w\s\*]*?\b(zs_\w+)\s*\(", text, flags=re.M)
+
+
+def status_string(status: int) -> str:
+    return load().zs_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != ZS_OK:
+        raise ZsError(fn, status)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtype: torch.dtype) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.contiguous()
+
+
+class Csr(NamedTuple):
+    rowptr: torch.Tensor   # (N+1,) int32
+    perm: torch.Tensor     # (E,) int32
+    dst32: torch.Tensor    # (E,) int32
+    n_nodes: int
+
+
+def zs_csr_workspace_bytes(n_edges: int, n_nodes: int) -> int:
+    return int(load().zs_csr_workspace_bytes(n_edges, n_nodes))
+
+
+def zs_build_csr(dst: torch.Tensor, n_nodes: int, workspace: torch.Tensor | None = None,
+                 out: Csr | None = None, bad_flag: torch.Tensor | None = None) -> Csr:
+    """Stable destination CSR of int64 ``dst``.
+
+    Without ``bad_flag`` the call synchronizes the stream and raises ZsError
+    (status ZS_ERR_INDEX) for a destination outside [0, n_nodes).  With a
+    one-element int32 GPU tensor ``bad_flag`` it returns at once and the flag
+    becomes nonzero, in stream order, if any destination was out of range.
+    """
+    dst = _dev_tensor(dst, "dst", torch.int64)
+    E = dst.numel()
+    dev = dst.device
+    if out is None:
+        out = Csr(torch.empty(n_nodes + 1, dtype=torch.int32, device=dev),
+                  torch.empty(E, dtype=torch.int32, device=dev),
+                  torch.empty(E, dtype=torch.int32, device=dev), n_nodes)
+    need = zs_csr_workspace_bytes(E, n_nodes)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("zs_build_csr", load().zs_build_csr(
+        _ptr(dst), E, n_nodes, _ptr(out.rowptr), _ptr(out.perm), _ptr(out.dst32),
+        _ptr(workspace), workspace.numel(), _ptr(bad_flag), _stream()))
+    return out
+
+
+def zs_forward(coupling: torch.Tensor, radial: torch.Tensor, csr: Csr,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """out (N, 16, C) fp32 with out[:, 0] = 0."""
+    coupling = _dev_tensor(coupling, "coupling", torch.float32)
+    radial = _dev_tensor(radial, "radial", torch.float32)
+    E = coupling.shape[0]
+    if coupling.shape != (E, ZONAL) or radial.dim() != 3 or radial.shape[:2] != (E, SLOTS):
+        raise ValueError("coupling must be (E, 15) and radial (E, 3, C)")
+    C = radial.shape[2]
+    if out is None:
+        out = torch.empty((csr.n_nodes, ROWS, C), dtype=torch.float32, device=coupling.device)
+    _check("zs_forward", load().zs_forward(
+        _ptr(coupling), _ptr(radial), _ptr(csr.rowptr), _ptr(csr.perm), csr.n_nodes, E, C,
+        _ptr(out), _stream()))
+    return out
+
+
+def zs_backward(grad_out: torch.Tensor, coupling: torch.Tensor, radial: torch.Tensor, csr: Csr,
+                grad_coupling: torch.Tensor | None = None,
+                grad_radial: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """(grad_coupling (E, 15), grad_radial (E, 3, C)) fp32."""
+    grad_out = _dev_tensor(grad_out, "grad_out", torch.float32)
+    coupling = _dev_tensor(coupling, "coupling", torch.float32)
+    radial = _dev_tensor(radial, "radial", torch.float32)
+    E, C = radial.shape[0], radial.shape[2]
+    if grad_out.shape != (csr.n_nodes, ROWS, C):
+        raise ValueError("grad_out must be (N, 16, C)")
+    if grad_coupling is None:
+        grad_coupling = torch.empty((E, ZONAL), dtype=torch.float32, device=radial.device)
+    if grad_radial is None:
+        grad_radial = torch.empty((E, SLOTS, C), dtype=torch.float32, device=radial.device)
+    _check("zs_backward", load().zs_backward(
+        _ptr(grad_out), _ptr(coupling), _ptr(radial), _ptr(csr.dst32), _ptr(csr.rowptr),
+        _ptr(csr.perm), csr.n_nodes, E, C, _ptr(grad_coupling), _ptr(grad_radial), _stream()))
+    return grad_coupling, grad_radial
+
+
+class _GieZonalScatter(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, coupling, radial, rowptr, perm, dst32, n_nodes):
+        csr = Csr(rowptr, perm, dst32, n_nodes)
+        ctx.save_for_backward(coupling, radial, rowptr, perm, dst32)
+        ctx.n_nodes = n_nodes
+        return zs_forward(coupling, radial, csr)
+
+    @staticmethod
+    @torch.autograd.function.once_differentiable
+    def backward(ctx, grad_out):
+        coupling, radial, rowptr, perm, dst32 = ctx.saved_tensors
+        csr = Csr(rowptr, perm, dst32, ctx.n_nodes)
+        gc, gr = zs_backward(grad_out.contiguous(), coupling, radial, csr)
+        return gc, gr, None, None, None, None
+
+
+def gie_zonal_scatter(coupling: torch.Tensor, radial: torch.Tensor, csr: Csr) -> torch.Tensor:
+    """Differentiable zonal scatter; inputs are made contiguous first."""
+    return _GieZonalScatter.apply(coupling.contiguous(), radial.contiguous(), csr.rowptr,
+                                  csr.perm, csr.dst32, csr.n_nodes)

@@ -1,0 +1,146 @@
+// C ABI of libzs (declared in include/zs.h): argument checks on the host, then
+// kernel dispatch.  Every check runs before the first HIP call, so a rejected
+// call leaves device state untouched.
+#include "zs.h"
+
+#include "zs_internal.h"
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range span(const void* p, int64_t count, size_t elem) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + uintptr_t(count) * elem};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool sizes_ok(int64_t n_edges, int64_t n_nodes) {
+    return n_edges >= 0 && n_edges <= ZS_MAX_EDGES && n_nodes >= 1 && n_nodes <= ZS_MAX_NODES;
+}
+
+bool channels_ok(int64_t c) { return c >= 1 && c <= ZS_MAX_CHANNELS; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ZS_OK : ZS_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* zs_status_string(int status) {
+    switch (status) {
+        case ZS_OK: return "ok";
+        case ZS_ERR_NULL: return "a required pointer is NULL";
+        case ZS_ERR_SHAPE: return "a size is out of the supported range";
+        case ZS_ERR_INDEX: return "a destination index is outside [0, n_nodes)";
+        case ZS_ERR_UNSUPPORTED: return "a pointer is not aligned to its element size";
+        case ZS_ERR_ALIAS: return "an output overlaps an input or another output";
+        case ZS_ERR_WORKSPACE: return "workspace is NULL or too small";
+        case ZS_ERR_HIP: return "a HIP runtime call failed";
+        default: return "unknown status";
+    }
+}
+
+size_t zs_csr_workspace_bytes(int64_t n_edges, int64_t n_nodes) {
+    if (!sizes_ok(n_edges, n_nodes)) return 0;
+    return zs::plan_csr(n_edges, n_nodes).bytes;
+}
+
+int zs_build_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* rowptr,
+                 int32_t* perm, int32_t* dst32, void* workspace, size_t workspace_bytes,
+                 int32_t* bad_flag, void* stream) {
+    if (!sizes_ok(n_edges, n_nodes)) return ZS_ERR_SHAPE;
+    if (!rowptr || (n_edges > 0 && (!dst || !perm || !dst32))) return ZS_ERR_NULL;
+    if (!aligned(rowptr, 4) || (n_edges > 0 && (!aligned(dst, 8) || !aligned(perm, 4) ||
+                                                !aligned(dst32, 4))))
+        return ZS_ERR_UNSUPPORTED;
+    if (bad_flag && !aligned(bad_flag, 4)) return ZS_ERR_UNSUPPORTED;
+    const Range r_dst = span(dst, n_edges, 8), r_rowptr = span(rowptr, n_nodes + 1, 4),
+                r_perm = span(perm, n_edges, 4), r_dst32 = span(dst32, n_edges, 4),
+                r_flag = span(bad_flag, bad_flag ? 1 : 0, 4);
+    if (overlap(r_rowptr, r_dst) || overlap(r_perm, r_dst) || overlap(r_dst32, r_dst) ||
+        overlap(r_rowptr, r_perm) || overlap(r_rowptr, r_dst32) || overlap(r_perm, r_dst32) ||
+        overlap(r_flag, r_dst) || overlap(r_flag, r_rowptr) || overlap(r_flag, r_perm) ||
+        overlap(r_flag, r_dst32))
+        return ZS_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (n_edges == 0) {
+        hipError_t err = zs::launch_fill_i32(rowptr, n_nodes + 1, 0, s);
+        if (err == hipSuccess && bad_flag) err = zs::launch_fill_i32(bad_flag, 1, 0, s);
+        return hip_status(err);
+    }
+    const zs::CsrPlan plan = zs::plan_csr(n_edges, n_nodes);
+    if (!workspace || workspace_bytes < plan.bytes) return ZS_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return ZS_ERR_UNSUPPORTED;
+    const Range r_ws = span(workspace, int64_t(plan.bytes), 1);
+    if (overlap(r_ws, r_dst) || overlap(r_ws, r_rowptr) || overlap(r_ws, r_perm) ||
+        overlap(r_ws, r_dst32) || overlap(r_ws, r_flag))
+        return ZS_ERR_ALIAS;
+    hipError_t err = zs::launch_csr(dst, n_edges, n_nodes, rowptr, perm, dst32, workspace, plan,
+                                    bad_flag, s);
+    if (err != hipSuccess) return ZS_ERR_HIP;
+    if (bad_flag) return ZS_OK;
+    int32_t flag = 0;
+    const int32_t* dflag = reinterpret_cast<const int32_t*>(static_cast<char*>(workspace) +
+                                                            plan.off_flag);
+    if (hipMemcpyAsync(&flag, dflag, sizeof(flag), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return ZS_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return ZS_ERR_HIP;
+    return flag ? ZS_ERR_INDEX : ZS_OK;
+}
+
+int zs_forward(const float* coupling, const float* radial, const int32_t* rowptr,
+               const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels, float* out,
+               void* stream) {
+    if (!sizes_ok(n_edges, n_nodes) || !channels_ok(channels)) return ZS_ERR_SHAPE;
+    if (!out || !rowptr || (n_edges > 0 && (!coupling || !radial || !perm))) return ZS_ERR_NULL;
+    if (!aligned(out, 4) || !aligned(rowptr, 4) ||
+        (n_edges > 0 && (!aligned(coupling, 4) || !aligned(radial, 4) || !aligned(perm, 4))))
+        return ZS_ERR_UNSUPPORTED;
+    const Range r_out = span(out, n_nodes * zs::kRows * channels, 4);
+    if (overlap(r_out, span(coupling, n_edges * zs::kZonal, 4)) ||
+        overlap(r_out, span(radial, n_edges * zs::kSlots * channels, 4)) ||
+        overlap(r_out, span(rowptr, n_nodes + 1, 4)) || overlap(r_out, span(perm, n_edges, 4)))
+        return ZS_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool vec4 = channels % 4 == 0 && aligned(out, 16) && (n_edges == 0 || aligned(radial, 16));
+    return hip_status(zs::launch_forward(coupling, radial, rowptr, perm, n_nodes, n_edges, channels,
+                                         out, vec4, s));
+}
+
+int zs_backward(const float* grad_out, const float* coupling, const float* radial,
+                const int32_t* dst32, const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
+                int64_t n_edges, int64_t channels, float* grad_coupling, float* grad_radial,
+                void* stream) {
+    if (!sizes_ok(n_edges, n_nodes) || !channels_ok(channels)) return ZS_ERR_SHAPE;
+    if (n_edges == 0) return ZS_OK;   // both gradients are empty
+    if (!grad_out || !coupling || !radial || !dst32 || !rowptr || !perm || !grad_coupling ||
+        !grad_radial)
+        return ZS_ERR_NULL;
+    if (!aligned(grad_out, 4) || !aligned(coupling, 4) || !aligned(radial, 4) ||
+        !aligned(dst32, 4) || !aligned(rowptr, 4) || !aligned(perm, 4) ||
+        !aligned(grad_coupling, 4) || !aligned(grad_radial, 4))
+        return ZS_ERR_UNSUPPORTED;
+    const Range r_gc = span(grad_coupling, n_edges * zs::kZonal, 4);
+    const Range r_gr = span(grad_radial, n_edges * zs::kSlots * channels, 4);
+    const Range ins[] = {span(grad_out, n_nodes * zs::kRows * channels, 4),
+                         span(coupling, n_edges * zs::kZonal, 4),
+                         span(radial, n_edges * zs::kSlots * channels, 4),
+                         span(dst32, n_edges, 4), span(rowptr, n_nodes + 1, 4),
+                         span(perm, n_edges, 4)};
+    if (overlap(r_gc, r_gr)) return ZS_ERR_ALIAS;
+    for (const Range& in : ins)
+        if (overlap(r_gc, in) || overlap(r_gr, in)) return ZS_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool vec4 = channels % 4 == 0 && aligned(grad_out, 16) && aligned(radial, 16) &&
+                      aligned(grad_radial, 16);
+    return hip_status(zs::launch_backward(grad_out, coupling, radial, dst32, rowptr, perm, n_nodes,
+                                          n_edges, channels, grad_coupling, grad_radial, vec4, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal declarations shared by the HIP translation units of libzs.
+// Not part of the public ABI (that is include/zs.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace zs {
+
+// Degree-slot of padded row r (1..15) for lmax = 3: the rows of degree l are
+// l*l .. l*l + 2l, so rows 1-3 -> slot 0, 4-8 -> slot 1, 9-15 -> slot 2.
+__host__ __device__ constexpr int row_slot(int r) { return r < 4 ? 0 : (r < 9 ? 1 : 2); }
+
+constexpr int kRows = 16;
+constexpr int kZonal = 15;
+constexpr int kSlots = 3;
+
+// Vector of VEC consecutive fp32 channels (VEC = 4: one 16-byte access).
+template <int VEC>
+struct VecT;
+template <>
+struct VecT<4> {
+    using T = float4;
+    __device__ static T load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+    __device__ static void store(float* p, const float (&v)[4]) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    __device__ static float get(const T& v, int i) {
+        return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+    }
+};
+template <>
+struct VecT<1> {
+    using T = float;
+    __device__ static T load(const float* p) { return *p; }
+    __device__ static void store(float* p, const float (&v)[1]) { *p = v[0]; }
+    __device__ static float get(const T& v, int) { return v; }
+};
+
+// ---- CSR build ------------------------------------------------------------
+struct CsrPlan {
+    int64_t tiles;        // number of edge tiles (one wavefront each in placement)
+    int64_t tile_edges;   // edges per tile (last tile may be shorter)
+    bool lds_bins;        // per-tile bins fit in LDS
+    size_t off_flag;      // int32 error flag
+    size_t off_counts;    // int32 [tiles][n_nodes] per-tile counts, then offsets
+    size_t off_blocks;    // int32 scan block sums
+    int64_t scan_blocks;
+    size_t bytes;         // total workspace bytes
+};
+CsrPlan plan_csr(int64_t n_edges, int64_t n_nodes);
+// flag: device int32 that receives the out-of-range indicator; NULL selects
+// the one inside the workspace (at plan.off_flag).
+hipError_t launch_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* rowptr,
+                      int32_t* perm, int32_t* dst32, void* workspace, const CsrPlan& plan,
+                      int32_t* flag, hipStream_t stream);
+
+// ---- forward / backward -----------------------------------------------------
+hipError_t launch_forward(const float* coupling, const float* radial, const int32_t* rowptr,
+                          const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels,
+                          float* out, bool vec4, hipStream_t stream);
+
+hipError_t launch_backward(const float* grad_out, const float* coupling, const float* radial,
+                           const int32_t* dst32, const int32_t* rowptr, const int32_t* perm,
+                           int64_t n_nodes, int64_t n_edges, int64_t channels,
+                           float* grad_coupling, float* grad_radial, bool vec4,
+                           hipStream_t stream);
+
+// Small fill kernel (used instead of hipMemsetAsync so the calls stay
+// capturable in HIP graphs).
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
+
+}  // namespace zs

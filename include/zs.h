@@ -1,0 +1,149 @@
+/*
+ * zs.h -- C ABI of the GIE zonal-scatter library for AMD Instinct MI355X
+ * (gfx950): the forward and backward of the geometric initial embedding's
+ * zonal scatter of the SeZM/DPA4 descriptor, plus the stable destination CSR
+ * both passes walk.
+ *
+ * Source of the operation: deepmd-kit PR #6072 ("fused Triton zonal scatter
+ * for the GIE head"), sections "What" and "Boundary and layout contract".
+ * With lmax = 3 the padded node layout has (lmax+1)^2 = 16 rows; row
+ * r = l*l + l + m (m = -l..l) belongs to degree l, giving row groups of 3/5/7
+ * rows for l = 1/2/3, and row 0 (l = 0) is the scalar row, always zero.
+ *
+ *   message[e][r][c] = coupling[e][r-1] * radial[e][l(r)-1][c]
+ *   out[n][r][c]     = sum over edges e with dst[e] == n of message[e][r][c]
+ *
+ * The fused operator never materialises the (E, 15, C) message surface.
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or retains them, and keeps no global state.
+ *  - Arrays are dense, row-major and contiguous; fp32 arrays must be 4-byte
+ *    aligned (16-byte alignment and C % 4 == 0 select the vector kernels).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *    stream), except zs_build_csr without a bad_flag, which synchronizes
+ *    `stream` once at the end to read back its index-validation flag.
+ *  - Inputs are never written.  Outputs must not overlap inputs or each other.
+ *  - Sizes: 0 <= n_edges <= ZS_MAX_EDGES, 1 <= n_nodes <= ZS_MAX_NODES,
+ *    1 <= channels <= ZS_MAX_CHANNELS.  n_edges == 0 is valid.
+ *  - Errors are negative return codes (zs_status); nothing is written when an
+ *    argument check fails.  Argument checks run on the host before any HIP
+ *    call, so a failing check touches no device state.
+ */
+#ifndef ZS_H_
+#define ZS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZS_LMAX 3
+#define ZS_ROWS 16          /* (ZS_LMAX + 1)^2 padded rows per node          */
+#define ZS_ZONAL 15         /* rows 1..15, one coupling column each           */
+#define ZS_SLOTS 3          /* radial slots, one per degree l = 1..ZS_LMAX    */
+#define ZS_MAX_CHANNELS 1024
+#define ZS_MAX_EDGES 2147483647LL  /* perm and rowptr hold int32 positions     */
+#define ZS_MAX_NODES 2147483646LL
+
+typedef enum zs_status {
+    ZS_OK = 0,
+    ZS_ERR_NULL = -1,        /* a required pointer is NULL                      */
+    ZS_ERR_SHAPE = -2,       /* a size is outside the ranges above              */
+    ZS_ERR_INDEX = -3,       /* a destination index is outside [0, n_nodes)     */
+    ZS_ERR_UNSUPPORTED = -4, /* an fp32/int32 pointer is not 4-byte aligned     */
+    ZS_ERR_ALIAS = -5,       /* an output overlaps an input or another output   */
+    ZS_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required         */
+    ZS_ERR_HIP = -7          /* a HIP runtime call (launch, copy, sync) failed  */
+} zs_status;
+
+/* Static, human-readable text for a status code; never NULL. */
+const char *zs_status_string(int status);
+
+/* Workspace bytes zs_build_csr needs for these sizes (0 if the sizes are out
+ * of range).  The workspace is scratch only; its contents need not be
+ * preserved between calls. */
+size_t zs_csr_workspace_bytes(int64_t n_edges, int64_t n_nodes);
+
+/*
+ * zs_build_csr -- stable destination CSR (same page, "What", last bullet: the
+ * fused forward walks the stable-sort CSR, whose per-node order is the edge
+ * order index_add uses).
+ *
+ *   dst      [n_edges]     int64  destination node of each edge (input)
+ *   rowptr   [n_nodes + 1] int32  rowptr[n] = #edges with dst < n (output)
+ *   perm     [n_edges]     int32  perm[k] = edge at sorted position k, edges of
+ *                                 equal dst in increasing edge id (output)
+ *   dst32    [n_edges]     int32  int32 copy of dst, -1 where out of range (output)
+ *   workspace, workspace_bytes >= zs_csr_workspace_bytes(n_edges, n_nodes),
+ *                                 256-byte aligned device scratch
+ *   bad_flag                      NULL: synchronous index check -- the call
+ *                                 synchronizes `stream` and returns ZS_ERR_INDEX
+ *                                 when any dst is outside [0, n_nodes).
+ *                                 Non-NULL (device int32): asynchronous -- the call
+ *                                 returns after enqueueing; when the stream
+ *                                 reaches the end of the build, *bad_flag is 0 if
+ *                                 every dst was in range and nonzero otherwise.
+ *
+ * Out-of-range destinations are never used as indices: the outputs are then
+ * unspecified, but no memory outside them, the workspace and bad_flag is
+ * written.
+ */
+int zs_build_csr(const int64_t *dst, int64_t n_edges, int64_t n_nodes,
+                 int32_t *rowptr, int32_t *perm, int32_t *dst32,
+                 void *workspace, size_t workspace_bytes, int32_t *bad_flag,
+                 void *stream);
+
+/*
+ * zs_forward -- fused zonal scatter forward (same page, "What", Forward
+ * bullet): one wavefront per node walks the node's CSR range in order and
+ * accumulates in registers.
+ *
+ *   coupling [n_edges][15]             fp32  zonal coupling (input)
+ *   radial   [n_edges][3][channels]    fp32  radial features, slot l-1 (input)
+ *   rowptr, perm                       from zs_build_csr for the same dst
+ *   out      [n_nodes][16][channels]   fp32  fully overwritten (output)
+ *
+ * out[n][0][:] = +0; out[n][r][c] adds fp32(coupling*radial) products over the
+ * node's edges in increasing edge id, starting from +0, with separate fp32
+ * multiply and add (no fused multiply-add): bitwise the fp32 result of the
+ * materialised message followed by index_add.  Run-to-run deterministic.
+ * A CSR that zs_build_csr did not produce gives unspecified values but no
+ * out-of-bounds access (positions and edge ids are range-checked).
+ */
+int zs_forward(const float *coupling, const float *radial,
+               const int32_t *rowptr, const int32_t *perm, int64_t n_nodes,
+               int64_t n_edges, int64_t channels, float *out, void *stream);
+
+/*
+ * zs_backward -- fused zonal scatter backward (same page, "What", Backward
+ * bullet): both operand gradients in a single edge-parallel pass, with no
+ * materialised message gradient.  Edges are visited grouped by destination
+ * (CSR order) so each node's upstream gradient rows are read once.
+ *
+ *   grad_out      [n_nodes][16][channels]  fp32  upstream gradient (row 0 unused)
+ *   coupling, radial                       as in zs_forward
+ *   dst32, rowptr, perm                    from zs_build_csr for the same dst
+ *   grad_coupling [n_edges][15]            fp32  fully overwritten (output)
+ *   grad_radial   [n_edges][3][channels]   fp32  fully overwritten (output)
+ *
+ * grad_radial[e][l-1][c] = sum over the rows r of degree l, in increasing r,
+ *   of fp32(grad_out[dst[e]][r][c] * coupling[e][r-1]), fp32 adds from +0.
+ * grad_coupling[e][r-1] = sum over c of grad_out[dst[e]][r][c] *
+ *   radial[e][l(r)-1][c], with exact products accumulated in fp64 and rounded
+ *   to fp32 once (equal to the correctly rounded sum except in rare near-ties,
+ *   where it may differ by one fp32 ulp).  Run-to-run deterministic.
+ */
+int zs_backward(const float *grad_out, const float *coupling,
+                const float *radial, const int32_t *dst32,
+                const int32_t *rowptr, const int32_t *perm, int64_t n_nodes,
+                int64_t n_edges, int64_t channels, float *grad_coupling,
+                float *grad_radial, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZS_H_ */

@@ -1,0 +1,101 @@
+"""The C ABI library: loads, exports what include/zs.h declares, and rejects bad
+arguments on the host before any HIP call (CPU only: no compute is launched)."""
+import ctypes
+import subprocess
+
+import pytest
+
+import edge_node_scatter_amd as zs
+
+ZS_ERR_NULL, ZS_ERR_SHAPE, ZS_ERR_INDEX = -1, -2, -3
+ZS_ERR_UNSUPPORTED, ZS_ERR_ALIAS, ZS_ERR_WORKSPACE = -4, -5, -6
+
+# Fake device addresses: every call below fails its host-side checks, so none
+# of these is ever dereferenced or handed to HIP.
+A = 0x7F0000000000
+B = 0x7F1000000000
+C_ = 0x7F2000000000
+D = 0x7F3000000000
+W = 0x7F4000000000
+X = 0x7F5000000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return zs.load()
+
+
+def test_header_symbols_exported(lib):
+    declared = zs.declared_symbols()
+    assert set(declared) == {"zs_status_string", "zs_csr_workspace_bytes", "zs_build_csr",
+                             "zs_forward", "zs_backward"}
+    out = subprocess.check_output(["nm", "-D", "--defined-only", zs.LIB_PATH], text=True)
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared:
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for s in range(-7, 1):
+        assert zs.status_string(s)
+    assert zs.status_string(-99) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert zs.zs_csr_workspace_bytes(-1, 10) == 0
+    assert zs.zs_csr_workspace_bytes(10, 0) == 0
+    assert zs.zs_csr_workspace_bytes(647170, 4096) >= 4096 * 4
+    assert zs.zs_csr_workspace_bytes(2600000, 16384) % 256 == 0
+
+
+def test_build_csr_rejects(lib):
+    def f(dst, e, n, rowptr, perm, dst32, ws, nbytes, flag=None):
+        return lib.zs_build_csr(dst, e, n, rowptr, perm, dst32, ws, nbytes, flag, None)
+    MB = 1 << 20
+    assert f(A, 10, 0, B, C_, D, W, MB) == ZS_ERR_SHAPE
+    assert f(A, -1, 4, B, C_, D, W, MB) == ZS_ERR_SHAPE
+    assert f(None, 10, 4, B, C_, D, W, MB) == ZS_ERR_NULL
+    assert f(A, 10, 4, None, C_, D, W, MB) == ZS_ERR_NULL
+    assert f(A + 4, 10, 4, B, C_, D, W, MB) == ZS_ERR_UNSUPPORTED   # int64 misaligned
+    assert f(A, 10, 4, B, C_, D, W, MB, X + 2) == ZS_ERR_UNSUPPORTED  # flag misaligned
+    assert f(A, 10, 4, A + 8, C_, D, W, MB) == ZS_ERR_ALIAS         # rowptr inside dst
+    assert f(A, 10, 4, B, B + 8, D, W, MB) == ZS_ERR_ALIAS          # perm over rowptr
+    assert f(A, 10, 4, B, C_, D, W, MB, C_ + 4) == ZS_ERR_ALIAS     # flag inside perm
+    assert f(A, 10, 4, B, C_, D, None, 0) == ZS_ERR_WORKSPACE
+    assert f(A, 10, 4, B, C_, D, W, 16) == ZS_ERR_WORKSPACE
+    assert f(A, 10, 4, B, C_, D, W + 4, MB) == ZS_ERR_UNSUPPORTED   # workspace alignment
+    assert f(A, 10, 4, B, C_, D, A, MB) == ZS_ERR_ALIAS            # workspace over dst
+    assert f(A, 10, 4, B, C_, D, W, MB, W + 64) == ZS_ERR_ALIAS     # flag inside workspace
+
+
+def test_forward_rejects(lib):
+    f = lib.zs_forward
+    assert f(A, B, C_, D, 4, 10, 0, X, None) == ZS_ERR_SHAPE
+    assert f(A, B, C_, D, 4, 10, 1025, X, None) == ZS_ERR_SHAPE
+    assert f(A, B, C_, D, 0, 10, 32, X, None) == ZS_ERR_SHAPE
+    assert f(A, B, C_, D, 4, -2, 32, X, None) == ZS_ERR_SHAPE
+    assert f(None, B, C_, D, 4, 10, 32, X, None) == ZS_ERR_NULL
+    assert f(A, B, C_, D, 4, 10, 32, None, None) == ZS_ERR_NULL
+    assert f(A, B + 2, C_, D, 4, 10, 32, X, None) == ZS_ERR_UNSUPPORTED
+    assert f(A, B, C_, D, 4, 10, 32, B + 64, None) == ZS_ERR_ALIAS            # out over radial
+    assert f(A, B, C_, D, 4, 10, 32, A, None) == ZS_ERR_ALIAS                 # out over coupling
+
+
+def test_backward_rejects(lib):
+    f = lib.zs_backward
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 10, 0, W, X, None) == ZS_ERR_SHAPE
+    assert f(None, B, C_, D, D + 4096, D + 8192, 4, 10, 32, W, X, None) == ZS_ERR_NULL
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 10, 32, W, None, None) == ZS_ERR_NULL
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 10, 32, W + 1, X, None) == ZS_ERR_UNSUPPORTED
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 10, 32, W, W + 16, None) == ZS_ERR_ALIAS
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 10, 32, A, X, None) == ZS_ERR_ALIAS
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 10, 32, W, C_ + 256, None) == ZS_ERR_ALIAS
+    # no edges: nothing to write, returns before touching the device
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 0, 32, W, X, None) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        zs.zs_build_csr(torch.zeros(3, dtype=torch.int64), 4)

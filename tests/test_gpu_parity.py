@@ -1,0 +1,281 @@
+"""HIP path vs the oracle, element by element, through the C ABI (needs a GPU).
+
+Bar (all configurations, same seeded inputs on both sides):
+  * CSR rowptr / perm / dst32: bitwise (integer work);
+  * forward out: bitwise (fixed edge order, separate fp32 multiply and add);
+  * grad_radial: bitwise (fixed row order);
+  * grad_coupling: |gpu - ref| <= 1e-6 + 1e-5 |ref| elementwise (the stated
+    fp32 tolerance); both sides sum exact products in fp64 and round once, so
+    at most a few near-ties may differ, by one fp32 ulp.
+The four smaller workloads are compared in full; the large one (E = 2.6M,
+C = 64) on sampled nodes and edges plus size-independent properties.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import edge_node_scatter_amd as zs
+import oracle
+import synthetic
+
+pytestmark = pytest.mark.gpu
+ATOL, RTOL = 1e-6, 1e-5
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    zs.load()
+    return torch.device("cuda:0")
+
+
+def _bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+def run_gpu(x, dev, n_nodes):
+    dst = torch.from_numpy(x["dst"]).to(dev)
+    cpl = torch.from_numpy(x["coupling"]).to(dev)
+    rad = torch.from_numpy(x["radial"]).to(dev)
+    g = torch.from_numpy(x["grad_out"]).to(dev)
+    csr = zs.zs_build_csr(dst, n_nodes)
+    out = zs.zs_forward(cpl, rad, csr)
+    gc, gr = zs.zs_backward(g, cpl, rad, csr)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in
+            dict(rowptr=csr.rowptr, perm=csr.perm, dst32=csr.dst32, out=out, gc=gc, gr=gr).items()}
+
+
+def check_grad_coupling(got, ref, what):
+    diff = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    tol = ATOL + RTOL * np.abs(ref.astype(np.float64))
+    assert np.all(diff <= tol), f"{what}: {np.count_nonzero(diff > tol)} outside tolerance"
+    nbits = np.count_nonzero(_bits(got) != _bits(ref))
+    ulps = np.abs(_bits(got).astype(np.int64) - _bits(ref).astype(np.int64))
+    assert nbits <= max(4, got.size // 100000), f"{what}: {nbits} bit differences"
+    assert np.all(ulps[_bits(got) != _bits(ref)] <= 1), f"{what}: difference above one ulp"
+    return nbits
+
+
+def compare_full(x, res, n_nodes, name):
+    rowptr, perm = oracle.csr(x["dst"], n_nodes)
+    assert np.array_equal(res["rowptr"], rowptr), f"{name}: rowptr"
+    assert np.array_equal(res["perm"], perm), f"{name}: perm"
+    assert np.array_equal(res["dst32"], x["dst"].astype(np.int32)), f"{name}: dst32"
+    out = oracle.forward(x["coupling"], x["radial"], x["dst"], n_nodes)
+    assert np.array_equal(_bits(res["out"]), _bits(out)), \
+        f"{name}: forward, {np.count_nonzero(_bits(res['out']) != _bits(out))} bit differences"
+    gc, gr = oracle.backward(x["grad_out"], x["coupling"], x["radial"], x["dst"])
+    assert np.array_equal(_bits(res["gr"]), _bits(gr)), \
+        f"{name}: grad_radial, {np.count_nonzero(_bits(res['gr']) != _bits(gr))} bit differences"
+    return check_grad_coupling(res["gc"], gc, f"{name}: grad_coupling")
+
+
+@pytest.mark.parametrize("name", ["tiny", "n1000", "headline", "skewed"])
+def test_workload_full(dev, name):
+    w = synthetic.WORKLOADS[name]
+    x = synthetic.make_inputs(w)
+    say(f"[gpu] workload {name}: N={w.n_nodes} E={w.n_edges} C={w.channels}")
+    res = run_gpu(x, dev, w.n_nodes)
+    nbits = compare_full(x, res, w.n_nodes, name)
+    say(f"[gpu] workload {name}: parity ok, grad_coupling bit differences {nbits}")
+
+
+def test_workload_large_sampled(dev):
+    w = synthetic.WORKLOADS["large"]
+    x = synthetic.make_inputs(w)
+    say(f"[gpu] workload large: N={w.n_nodes} E={w.n_edges} C={w.channels}")
+    res = run_gpu(x, dev, w.n_nodes)
+    rowptr, perm = oracle.csr(x["dst"], w.n_nodes)
+    assert np.array_equal(res["rowptr"], rowptr) and np.array_equal(res["perm"], perm)
+    rng = np.random.default_rng(1)
+    nodes = np.concatenate([[0, w.n_nodes - 1], rng.choice(w.n_nodes, 62, replace=False)])
+    ref_rows = oracle.forward_nodes(x["coupling"], x["radial"], x["dst"], w.n_nodes, nodes)
+    assert np.array_equal(_bits(res["out"][nodes]), _bits(ref_rows)), "large: sampled forward rows"
+    edges = np.concatenate([[0, w.n_edges - 1], rng.choice(w.n_edges, 20000, replace=False)])
+    gc, gr = oracle.backward_edges(x["grad_out"], x["coupling"], x["radial"], x["dst"], edges)
+    assert np.array_equal(_bits(res["gr"][edges]), _bits(gr)), "large: sampled grad_radial"
+    check_grad_coupling(res["gc"][edges], gc, "large: sampled grad_coupling")
+    # size-independent properties over the whole output
+    assert np.all(_bits(res["out"][:, 0]) == 0), "row 0 must be +0"
+    deg = np.bincount(x["dst"], minlength=w.n_nodes)
+    for r in (1, 5, 12):
+        s = 0 if r < 4 else (1 if r < 9 else 2)
+        tot = x["coupling"][:, r - 1].astype(np.float64) @ x["radial"][:, s, :].astype(np.float64)
+        got = res["out"][:, r, :].astype(np.float64).sum(axis=0)
+        scale = np.abs(x["coupling"][:, r - 1]).astype(np.float64) @ \
+            np.abs(x["radial"][:, s, :]).astype(np.float64)
+        assert np.all(np.abs(got - tot) <= (deg.max() + 2) * 2.0 ** -24 * scale + 1e-30), \
+            f"large: total message row {r}"
+
+
+def test_deterministic_headline(dev):
+    w = synthetic.WORKLOADS["headline"]
+    x = synthetic.make_inputs(w)
+    say("[gpu] determinism: headline x10")
+    first = run_gpu(x, dev, w.n_nodes)
+    for _ in range(9):
+        again = run_gpu(x, dev, w.n_nodes)
+        for k in first:
+            assert np.array_equal(first[k].view(np.uint8), again[k].view(np.uint8)), k
+
+
+EDGE_CASES = [
+    # (label, N, E, C, dst kind)
+    ("one_edge", 5, 1, 32, "uniform"),
+    ("one_node", 1, 3001, 32, "uniform"),
+    ("e37", 9, 37, 32, "uniform"),
+    ("e63", 7, 63, 16, "uniform"),
+    ("e64", 7, 64, 8, "uniform"),
+    ("e65", 7, 65, 4, "uniform"),
+    ("tile_2047", 40, 2047, 32, "uniform"),
+    ("tile_2048", 40, 2048, 32, "uniform"),
+    ("tile_2049", 40, 2049, 32, "uniform"),
+    ("e8193", 300, 8193, 32, "uniform"),
+    ("mostly_empty", 5000, 300, 32, "uniform"),
+    ("c1", 17, 500, 1, "uniform"),
+    ("c2", 17, 500, 2, "uniform"),
+    ("c3", 17, 500, 3, "uniform"),
+    ("c5", 17, 500, 5, "uniform"),
+    ("c31", 17, 500, 31, "uniform"),
+    ("c33", 17, 500, 33, "uniform"),
+    ("c36", 17, 500, 36, "uniform"),
+    ("c40_pages", 33, 777, 40, "uniform"),
+    ("c63", 17, 500, 63, "uniform"),
+    ("c64", 17, 500, 64, "uniform"),
+    ("c65", 17, 500, 65, "uniform"),
+    ("c96", 17, 500, 96, "uniform"),
+    ("c128", 17, 700, 128, "uniform"),
+    ("c260", 9, 300, 260, "uniform"),
+    ("c1024", 3, 70, 1024, "uniform"),
+    ("skew_small", 200, 9000, 32, "skewed_small"),
+    ("nodes_20000", 20000, 40000, 8, "uniform"),      # global-bin CSR path (N > 16384)
+]
+
+
+@pytest.mark.parametrize("label,N,E,C,kind", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
+def test_edge_cases(dev, label, N, E, C, kind):
+    w = synthetic.custom(label, N, E, C, seed=1000 + len(label) * 7 + C, envelope=True)
+    x = synthetic.make_inputs(w)
+    if kind == "skewed_small":
+        rng = np.random.default_rng(5)
+        x["dst"] = np.where(rng.random(E) < 0.7, rng.integers(0, 10, E), rng.integers(0, N, E))
+    say(f"[gpu] edge case {label}: N={N} E={E} C={C}")
+    res = run_gpu(x, dev, N)
+    compare_full(x, res, N, label)
+
+
+def test_all_edges_one_node(dev):
+    N, E, C = 50, 20000, 32
+    w = synthetic.custom("hub", N, E, C, seed=77)
+    x = synthetic.make_inputs(w)
+    x["dst"] = np.full(E, 7, dtype=np.int64)
+    say("[gpu] hub node: all 20000 edges on node 7")
+    res = run_gpu(x, dev, N)
+    compare_full(x, res, N, "hub")
+
+
+def test_no_edges(dev):
+    say("[gpu] E = 0")
+    N, C = 6, 32
+    dst = torch.zeros(0, dtype=torch.int64, device=dev)
+    cpl = torch.zeros((0, 15), device=dev)
+    rad = torch.zeros((0, 3, C), device=dev)
+    csr = zs.zs_build_csr(dst, N)
+    out = zs.zs_forward(cpl, rad, csr, out=torch.full((N, 16, C), float("nan"), device=dev))
+    gc, gr = zs.zs_backward(torch.ones((N, 16, C), device=dev), cpl, rad, csr)
+    torch.cuda.synchronize()
+    assert torch.equal(csr.rowptr.cpu(), torch.zeros(N + 1, dtype=torch.int32))
+    assert np.all(_bits(out.cpu().numpy()) == 0)
+    assert gc.shape == (0, 15) and gr.shape == (0, 3, C)
+
+
+def test_bad_destination_rejected(dev):
+    N, E = 10, 5000
+    for bad in (N, -1, 1 << 40):
+        say(f"[gpu] bad destination {bad}")
+        d = torch.zeros(E, dtype=torch.int64)
+        d[E // 3] = bad
+        with pytest.raises(zs.ZsError) as ei:
+            zs.zs_build_csr(d.to(dev), N)
+        assert ei.value.status == -3
+
+
+def test_guard_regions_and_unaligned(dev):
+    """Outputs inside NaN-poisoned buffers: nothing outside them is written and
+    nothing past the inputs is read; a one-float offset takes the scalar path."""
+    E, N, C = 777, 33, 40                      # the pages' non-power-of-two case
+    w = synthetic.custom("guard", N, E, C, seed=4040)
+    x = synthetic.make_inputs(w)
+    ref_out = oracle.forward(x["coupling"], x["radial"], x["dst"], N)
+    ref_gc, ref_gr = oracle.backward(x["grad_out"], x["coupling"], x["radial"], x["dst"])
+    for off in (0, 1):
+        say(f"[gpu] guard regions, offset {off}")
+        G = 4096
+
+        def poisoned(arr):
+            buf = torch.full((off + arr.size + G,), float("nan"), device=dev)
+            buf[off:off + arr.size] = torch.from_numpy(arr.ravel()).to(dev)
+            return buf, buf[off:off + arr.size].view(arr.shape)
+
+        _, cpl = poisoned(x["coupling"])
+        _, rad = poisoned(x["radial"])
+        _, g = poisoned(x["grad_out"])
+        csr = zs.zs_build_csr(torch.from_numpy(x["dst"]).to(dev), N)
+        obuf = torch.full((off + N * 16 * C + G,), float("nan"), device=dev)
+        out = obuf[off:off + N * 16 * C].view(N, 16, C)
+        gcbuf = torch.full((off + E * 15 + G,), float("nan"), device=dev)
+        grbuf = torch.full((off + E * 3 * C + G,), float("nan"), device=dev)
+        gc = gcbuf[off:off + E * 15].view(E, 15)
+        gr = grbuf[off:off + E * 3 * C].view(E, 3, C)
+        zs.zs_forward(cpl, rad, csr, out=out)
+        zs.zs_backward(g, cpl, rad, csr, grad_coupling=gc, grad_radial=gr)
+        torch.cuda.synchronize()
+        for buf, n in ((obuf, N * 16 * C), (gcbuf, E * 15), (grbuf, E * 3 * C)):
+            b = buf.cpu().numpy()
+            assert np.all(np.isnan(b[:off])) and np.all(np.isnan(b[off + n:])), "write outside output"
+        assert np.array_equal(_bits(out.cpu().numpy()), _bits(ref_out))
+        assert np.array_equal(_bits(gr.cpu().numpy()), _bits(ref_gr))
+        check_grad_coupling(gc.cpu().numpy(), ref_gc, "guard grad_coupling")
+
+
+def test_inputs_not_modified(dev):
+    w = synthetic.custom("immut", 100, 5000, 32, seed=9)
+    x = synthetic.make_inputs(w)
+    say("[gpu] inputs unchanged")
+    t = {k: torch.from_numpy(x[k]).to(dev) for k in ("dst", "coupling", "radial", "grad_out")}
+    before = {k: v.clone() for k, v in t.items()}
+    csr = zs.zs_build_csr(t["dst"], 100)
+    zs.zs_forward(t["coupling"], t["radial"], csr)
+    zs.zs_backward(t["grad_out"], t["coupling"], t["radial"], csr)
+    torch.cuda.synchronize()
+    for k in t:
+        assert torch.equal(t[k], before[k]), k
+
+
+def test_autograd_function_sliced_radial(dev):
+    """The autograd wrapper (contiguous and sliced-view radial) against the oracle."""
+    w = synthetic.custom("autograd", 40, 3000, 32, seed=31)
+    x = synthetic.make_inputs(w)
+    say("[gpu] autograd wrapper")
+    csr = zs.zs_build_csr(torch.from_numpy(x["dst"]).to(dev), 40)
+    ref_out = oracle.forward(x["coupling"], x["radial"], x["dst"], 40)
+    ref_gc, ref_gr = oracle.backward(x["grad_out"], x["coupling"], x["radial"], x["dst"])
+    wide = torch.randn((3000, 5, 32), device=dev)
+    wide[:, 1:4] = torch.from_numpy(x["radial"]).to(dev)
+    for rad in (torch.from_numpy(x["radial"]).to(dev), wide[:, 1:4]):
+        cpl = torch.from_numpy(x["coupling"]).to(dev).requires_grad_(True)
+        rad = rad.detach().requires_grad_(True)
+        out = zs.gie_zonal_scatter(cpl, rad, csr)
+        out.backward(torch.from_numpy(x["grad_out"]).to(dev))
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(out.detach().cpu().numpy()), _bits(ref_out))
+        assert np.array_equal(_bits(rad.grad.cpu().numpy()), _bits(ref_gr))
+        check_grad_coupling(cpl.grad.cpu().numpy(), ref_gc, "autograd grad_coupling")
