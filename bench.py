@@ -36,9 +36,15 @@ import synthetic  # noqa: E402
 
 METRIC = "zonal scatter fwd+bwd µs and HBM GB/s (% peak) at N=4096,E=647170,C=32"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published peak
+COPY_CALIBRATION_BYTES = 256 * 1024 * 1024   # bytes read (and written) by the calibration copy
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_headline.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "edge_node_scatter_amd", "csrc", f)
-                  for f in ("zs_fwd.hip", "zs_bwd.hip", "zs_csr.hip", "zs_internal.h")]
+_CSRC = os.path.join(ROOT, "edge_node_scatter_amd", "csrc")
+# Sources that determine each kernel family's code (compiler flags live in build.py).
+KERNEL_SOURCES = {
+    "fwd": ["zs_fwd.hip", "zs_internal.h"],
+    "bwd": ["zs_bwd.hip", "zs_internal.h"],
+    "csr": ["zs_csr.hip", "zs_internal.h"],
+}
 
 
 def algorithmic_bytes(n_edges: int, n_nodes: int, channels: int) -> dict:
@@ -58,12 +64,18 @@ def algorithmic_bytes(n_edges: int, n_nodes: int, channels: int) -> dict:
     return {"fwd": fwd, "bwd": bwd, "build": build}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(family: str | None = None) -> str:
+    """Hash of the sources (and build flags) of one kernel family, or of all."""
+    files = sorted({f for fam, fs in KERNEL_SOURCES.items() if family in (None, fam) for f in fs})
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
+    for name in files + [os.path.join("..", "build.py")]:
+        with open(os.path.join(_CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def _family(kernel: str) -> str:
+    return "fwd" if "fwd" in kernel else ("bwd" if "bwd" in kernel else "csr")
 
 
 def load_traffic(kernel: str, n_calls_per_step: int = 1):
@@ -74,12 +86,63 @@ def load_traffic(kernel: str, n_calls_per_step: int = 1):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != kernel_source_hash():
-        return None
     k = t.get("kernels", {}).get(kernel)
-    if not k:
+    if not k or k.get("source_hash") != kernel_source_hash(_family(kernel)):
         return None
     return k.get("hbm_bytes_per_launch")
+
+
+def _kernel_short_name(name: str) -> str:
+    return name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+def write_traffic(fetch_csv: str, write_csv: str) -> dict:
+    """Per-kernel HBM bytes per launch from two rocprofv3 --pmc runs of
+    ``bench.py --calibrate-copy`` (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch), each scaled by what the same counter reads for the plain
+    256 MiB device copy of the same run.  Writes profiles/traffic_headline.json
+    and returns it."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        vals = collections.defaultdict(list)
+        copies = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                kib = float(r["Counter_Value"])
+                name = _kernel_short_name(r["Kernel_Name"])
+                if "copyBuffer" in name and kib > COPY_CALIBRATION_BYTES / 1024 / 8:
+                    copies.append(kib)
+                elif name.startswith("zs::"):
+                    vals[name].append(kib)
+        if not copies:
+            raise RuntimeError(f"{path}: no calibration copy found")
+        scale = (COPY_CALIBRATION_BYTES / 1024) / statistics.median(copies)
+        return {k: statistics.fmean(v) for k, v in vals.items()}, scale, copies
+
+    fetch, fscale, fcopies = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, wscale, wcopies = per_kernel(write_csv, "WRITE_SIZE")
+    kernels = {}
+    for name in sorted(set(fetch) | set(write)):
+        fb = fetch.get(name, 0.0) * 1024 * fscale
+        wb = write.get(name, 0.0) * 1024 * wscale
+        key = name.split("::")[-1].split("<")[0]
+        kernels.setdefault(key, {})[name] = {
+            "source_hash": kernel_source_hash(_family(key)),
+            "fetch_kib_raw": round(fetch.get(name, 0.0), 1),
+            "write_kib_raw": round(write.get(name, 0.0), 1),
+            "fetch_bytes": round(fb), "write_bytes": round(wb),
+            "hbm_bytes_per_launch": round(fb + wb)}
+    out = {"fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5),
+           "calibration_copy_bytes": COPY_CALIBRATION_BYTES,
+           "calibration_fetch_kib_raw": fcopies, "calibration_write_kib_raw": wcopies,
+           "kernels": {k: (list(v.values())[0] if len(v) == 1 else v) for k, v in kernels.items()}}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
 
 
 def cpu_baseline(x, w, budget_s: float = 12.0) -> dict:
@@ -114,7 +177,16 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline", choices=sorted(synthetic.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarize two rocprofv3 --pmc counter_collection.csv files "
+                         "(FETCH_SIZE, WRITE_SIZE) into profiles/traffic_headline.json and exit")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run a plain 256 MiB device copy three times "
+                         "(reference kernel for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
+    if args.write_traffic:
+        print(json.dumps(write_traffic(*args.write_traffic), indent=1))
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by destination node with no exchange, see the design notes)",
@@ -180,7 +252,7 @@ def main() -> int:
     fb_us = fwd_us + bwd_us
     gbs = (nb["fwd"] + nb["bwd"]) / (fb_us * 1e-6) / 1e9
     bwd_gbs = nb["bwd"] / (bwd_us * 1e-6) / 1e9
-    traffic = load_traffic("zs_bwd_kernel")
+    traffic = load_traffic("zs_bwd_staged_kernel")
 
     rec = {
         "metric": METRIC,
@@ -208,7 +280,7 @@ def main() -> int:
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": nb,
         "roofline": {
-            "kernel": "zs_bwd_kernel",
+            "kernel": "zs_bwd_staged_kernel",
             "bound": "hbm",
             "achieved": round(bwd_gbs, 1),
             "peak": PEAK_HBM_GBS,
@@ -218,8 +290,15 @@ def main() -> int:
             "algorithmic_bytes_per_launch": nb["bwd"],
             "avg_launch_us": round(bwd_us, 2),
         },
-        "source_hash": kernel_source_hash(),
+        "source_hash": {fam: kernel_source_hash(fam) for fam in KERNEL_SOURCES},
     }
+    if args.calibrate_copy:
+        src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst_copy = torch.empty_like(src)
+        for _ in range(3):
+            dst_copy.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = COPY_CALIBRATION_BYTES
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x, w)
     print(json.dumps(rec), flush=True)

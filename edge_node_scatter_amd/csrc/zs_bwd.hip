@@ -184,6 +184,257 @@ __global__ __launch_bounds__(256) void zs_bwd_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Staged backward for C <= 4*NQ, C % 4 == 0, 16-byte aligned grad_out, radial
+// and grad_radial.  One wavefront per node; lane = b*NQ + q handles channels
+// 4q..4q+3 of edge slot b (EPW = 64/NQ edges per step).
+//
+//  - The node's upstream rows g[n][1..15] are staged in LDS once and re-read
+//    every step (holding them and their fp64 conversions in registers across
+//    steps would need ~180 registers).
+//  - Each step's perm entries are fetched two steps ahead; its radial float4s
+//    (three per lane) and its coupling rows (EPW x 15 floats, fetched with
+//    coalesced all-distinct loads, at most two per lane) one step ahead into
+//    one of two register buffers, so loads overlap the previous step's math.
+//    The coupling floats go through LDS so every lane of an edge gets the
+//    edge's 15 weights.
+//  - The 15 row sums of grad_coupling are reduced in two rounds (rows 1-8 of
+//    degrees 1 and 2, then rows 9-15 of degree 3), 8 values each, by
+//    recursive halving with DPP lane exchanges inside each 8- or 16-lane
+//    edge group.
+// Arithmetic is that of zs_bwd_kernel.
+// ---------------------------------------------------------------------------
+template <int NQ>
+struct BwdRegs {
+    static constexpr int EPW = 64 / NQ;
+    static constexpr int CPL = (EPW * kZonal + 63) / 64;   // coupling floats per lane
+    float4 x[kSlots];
+    float w[CPL];
+};
+
+__device__ __attribute__((always_inline)) inline int bwd_perm(const int32_t* __restrict__ perm,
+                                                              int64_t k, int64_t k1,
+                                                              int64_t n_edges) {
+    int32_t e = -1;
+    if (k < k1) {
+        e = perm[k];
+        if (e < 0 || e >= n_edges) e = -1;
+    }
+    return e;
+}
+
+template <int NQ>
+__device__ __attribute__((always_inline)) inline void bwd_fetch(BwdRegs<NQ>& R, int e, int lane,
+                                                                 bool cact, int64_t c0,
+                                                                 const float* __restrict__ coupling,
+                                                                 const float* __restrict__ radial,
+                                                                 int64_t C) {
+    constexpr int EPW = BwdRegs<NQ>::EPW;
+    const int64_t row_stride = int64_t(kSlots) * C;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (e >= 0 && cact)
+            v = load_stream4<ZS_BWD_NT != 0>(radial + int64_t(e) * row_stride + s * C + c0);
+        R.x[s] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < BwdRegs<NQ>::CPL; ++i) {
+        const int idx = i * 64 + lane;               // coupling float of this step
+        const bool in = idx < EPW * kZonal;
+        const int owner = (in ? idx / kZonal : 0) * NQ;   // a lane of that edge slot
+        const int ee = __shfl(e, owner, 64);
+        float v = 0.0f;
+        if (in && ee >= 0) v = coupling[int64_t(ee) * kZonal + idx % kZonal];
+        R.w[i] = v;
+    }
+}
+
+__device__ __attribute__((always_inline)) inline float comp(const float4& v, int i) {
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// Lane exchange of a double inside a 16-lane DPP row.
+template <int CTRL>
+__device__ __attribute__((always_inline)) inline double dpp_f64(double v) {
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+
+// DPP controls: partner of lane q (within its aligned group) at halving step H.
+//   H = 8: row_mirror (q <-> 15 - q), H = 4: row_half_mirror (q <-> 7 - q),
+//   H = 2: quad_perm [2,3,0,1] (q ^ 2), H = 1: quad_perm [1,0,3,2] (q ^ 1).
+// Each pairs a lane with bit H set with one that has it clear, so "up" = q & H.
+template <int H>
+struct PartnerCtrl;
+template <> struct PartnerCtrl<8> { static constexpr int v = 0x140; };
+template <> struct PartnerCtrl<4> { static constexpr int v = 0x141; };
+template <> struct PartnerCtrl<2> { static constexpr int v = 0x4E; };   // [2,3,0,1]
+template <> struct PartnerCtrl<1> { static constexpr int v = 0xB1; };   // [1,0,3,2]
+
+template <int H, int CNT>
+struct Halving8 {
+    __device__ __attribute__((always_inline)) static void run(double (&v)[8], int q, int& base) {
+        constexpr int half = CNT / 2;
+        const bool up = (q & H) != 0;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const double keep = up ? v[i + half] : v[i];
+            const double send = up ? v[i] : v[i + half];
+            v[i] = keep + dpp_f64<PartnerCtrl<H>::v>(send);
+        }
+        if (up) base += half;
+        Halving8<H / 2, half>::run(v, q, base);
+    }
+};
+template <int CNT>
+struct Halving8<0, CNT> {
+    __device__ static void run(double (&)[8], int, int&) {}
+};
+
+// 8 fp64 row partials -> one row sum per lane, over the NQ lanes of an edge.
+template <int NQ>
+__device__ __attribute__((always_inline)) inline double reduce8(double (&v)[8], int q, int& base) {
+    base = 0;
+    if (NQ == 16) {
+        Halving8<8, 8>::run(v, q, base);                  // steps 8, 4, 2
+        return v[0] + dpp_f64<PartnerCtrl<1>::v>(v[0]);   // both of a pair hold the sum
+    } else {
+        Halving8<4, 8>::run(v, q, base);                  // steps 4, 2, 1
+        return v[0];
+    }
+}
+
+template <int NQ>
+__device__ __attribute__((always_inline)) inline void bwd_compute(
+    const BwdRegs<NQ>& R, int e, int lane, int b, bool cact, int64_t c0, int q,
+    const float4* gsh, float* wsh, int64_t C, float* __restrict__ grad_coupling,
+    float* __restrict__ grad_radial) {
+    constexpr int EPW = BwdRegs<NQ>::EPW;
+    // stage this step's coupling rows, then read the 15 weights of edge slot b
+#pragma unroll
+    for (int i = 0; i < BwdRegs<NQ>::CPL; ++i) {
+        const int idx = i * 64 + lane;
+        if (idx < EPW * kZonal) wsh[(idx / kZonal) * 16 + idx % kZonal] = R.w[i];
+    }
+    float w[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 t = reinterpret_cast<const float4*>(wsh + b * 16)[i];
+        w[4 * i] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
+    }
+    const bool ok = e >= 0;
+    const bool act = ok && cact;
+    const int64_t row_stride = int64_t(kSlots) * C;
+    float* grow = grad_radial + int64_t(ok ? e : 0) * row_stride + c0;
+    float* gcrow = grad_coupling + int64_t(ok ? e : 0) * kZonal;
+#pragma unroll
+    for (int round = 0; round < 2; ++round) {
+        // Re-read the staged rows every step (see above).
+        __asm__ volatile("" ::: "memory");
+        const int r_lo = round == 0 ? 1 : 9;
+        const int r_hi = round == 0 ? 8 : 15;
+        double part[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part[i] = 0.0;
+        float acc[kSlots][4];
+#pragma unroll
+        for (int s = 0; s < kSlots; ++s)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[s][v] = 0.0f;
+#pragma unroll
+        for (int r = r_lo; r <= r_hi; ++r) {
+            const float4 g = gsh[(r - 1) * NQ + q];
+            const int s = row_slot(r);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float p = comp(g, v) * w[r - 1];
+                acc[s][v] = acc[s][v] + p;
+                part[r - r_lo] = __builtin_fma(double(comp(g, v)), double(comp(R.x[s], v)),
+                                               part[r - r_lo]);
+            }
+        }
+        if (act) {
+#pragma unroll
+            for (int s = 0; s < kSlots; ++s)
+                if (row_slot(r_lo) <= s && s <= row_slot(r_hi))
+                    store_stream4<ZS_BWD_NT != 0>(grow + s * C,
+                                  make_float4(acc[s][0], acc[s][1], acc[s][2], acc[s][3]));
+        }
+        int base;
+        const double sum = reduce8<NQ>(part, q, base);
+        const int col = r_lo - 1 + base;
+        if (ok && col <= r_hi - 1 && (NQ == 8 || (q & 1) == 0)) gcrow[col] = float(sum);
+    }
+}
+
+// Occupancy request for the staged backward (build-time tuning knob).
+#ifndef ZS_BWD_WAVES_PER_EU
+#define ZS_BWD_WAVES_PER_EU 4
+#endif
+#if ZS_BWD_WAVES_PER_EU > 0
+#define ZS_BWD_OCCUPANCY __attribute__((amdgpu_waves_per_eu(ZS_BWD_WAVES_PER_EU)))
+#else
+#define ZS_BWD_OCCUPANCY
+#endif
+
+template <int NQ>
+__global__ __launch_bounds__(64) ZS_BWD_OCCUPANCY void zs_bwd_staged_kernel(
+    const float* __restrict__ grad_out, const float* __restrict__ coupling,
+    const float* __restrict__ radial, const int32_t* __restrict__ rowptr,
+    const int32_t* __restrict__ perm, int64_t n_nodes, int64_t n_edges, int64_t C,
+    float* __restrict__ grad_coupling, float* __restrict__ grad_radial) {
+    constexpr int EPW = 64 / NQ;
+    __shared__ float4 gsh[kZonal * NQ];
+    __shared__ float4 wsh4[EPW * 4];
+    float* wsh = reinterpret_cast<float*>(wsh4);
+    const int lane = threadIdx.x;
+    const int q = lane % NQ;
+    const int b = lane / NQ;
+    const int64_t c0 = int64_t(q) * 4;
+    const bool cact = c0 < C;
+    if (lane < EPW) wsh[lane * 16 + 15] = 0.0f;     // pad column, never fetched
+
+    for (int64_t node = blockIdx.x; node < n_nodes; node += gridDim.x) {
+        int64_t k0 = rowptr[node];
+        int64_t k1 = rowptr[node + 1];
+        k0 = k0 < 0 ? 0 : (k0 > n_edges ? n_edges : k0);
+        k1 = k1 < k0 ? k0 : (k1 > n_edges ? n_edges : k1);
+        if (k0 >= k1) continue;
+        const float* gnode = grad_out + node * kRows * C;
+        for (int i = lane; i < kZonal * NQ; i += 64) {
+            const int r = i / NQ + 1;
+            const int64_t c = int64_t(i % NQ) * 4;
+            float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (c < C) v = *reinterpret_cast<const float4*>(gnode + int64_t(r) * C + c);
+            gsh[i] = v;
+        }
+        const int64_t nsteps = (k1 - k0 + EPW - 1) / EPW;
+        BwdRegs<NQ> A, B;
+        int eA = bwd_perm(perm, k0 + b, k1, n_edges);
+        int pB = bwd_perm(perm, k0 + EPW + b, k1, n_edges);
+        int eB = -1;
+        bwd_fetch<NQ>(A, eA, lane, cact, c0, coupling, radial, C);
+        for (int64_t t = 0; t < nsteps; t += 2) {
+            const int pN = bwd_perm(perm, k0 + (t + 2) * EPW + b, k1, n_edges);
+            if (t + 1 < nsteps) {
+                bwd_fetch<NQ>(B, pB, lane, cact, c0, coupling, radial, C);
+                eB = pB;
+            }
+            bwd_compute<NQ>(A, eA, lane, b, cact, c0, q, gsh, wsh, C, grad_coupling, grad_radial);
+            if (t + 1 >= nsteps) break;
+            pB = bwd_perm(perm, k0 + (t + 3) * EPW + b, k1, n_edges);
+            if (t + 2 < nsteps) {
+                bwd_fetch<NQ>(A, pN, lane, cact, c0, coupling, radial, C);
+                eA = pN;
+            }
+            bwd_compute<NQ>(B, eB, lane, b, cact, c0, q, gsh, wsh, C, grad_coupling, grad_radial);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_backward(const float* grad_out, const float* coupling, const float* radial,
@@ -200,9 +451,13 @@ hipError_t launch_backward(const float* grad_out, const float* coupling, const f
                                                          grad_coupling, grad_radial)
     if (vec4) {
         if (channels <= 32)
-            ZS_BWD_LAUNCH(4, 8, true);
+            zs_bwd_staged_kernel<8><<<gx, 64, 0, stream>>>(grad_out, coupling, radial, rowptr,
+                                                           perm, n_nodes, n_edges, channels,
+                                                           grad_coupling, grad_radial);
         else if (channels <= 64)
-            ZS_BWD_LAUNCH(4, 16, true);
+            zs_bwd_staged_kernel<16><<<gx, 64, 0, stream>>>(grad_out, coupling, radial, rowptr,
+                                                            perm, n_nodes, n_edges, channels,
+                                                            grad_coupling, grad_radial);
         else
             ZS_BWD_LAUNCH(4, 16, false);
     } else {

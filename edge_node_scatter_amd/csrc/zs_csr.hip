@@ -3,21 +3,25 @@
 // The fused forward walks each node's edges in the order index_add would add
 // them, i.e. increasing edge id (deepmd-kit PR #6072, "fused Triton zonal
 // scatter for the GIE head", section "What", last bullet).  This file builds
-// that CSR with a deterministic counting sort; no step depends on the order in
-// which atomics land:
+// that CSR with a deterministic counting sort; no result depends on the order
+// in which atomics land:
 //
-//   1. count   one workgroup per edge tile histograms its destinations
-//              (LDS bins when N fits, else the tile's own global row);
-//   2. colscan per node, an exclusive scan of the per-tile counts over tiles
-//              (tile-major offsets) and the node's degree;
+//   1. count   one workgroup per edge tile histograms its destinations (LDS
+//              bins when N fits, else the tile's own global row) and records
+//              whether the tile held an out-of-range destination;
+//   2. colscan per node, the exclusive scan of the per-tile counts over tiles
+//              (tile-major offsets) and the node's degree; 8 threads share a
+//              node's tiles, so the scan runs on N*8 threads;
 //   3. scan    exclusive scan of degrees over nodes -> rowptr;
-//   4. place   one wavefront per tile walks its edges in increasing id, 64 at a
-//              time; lanes with equal keys are matched with ballots, ranked by
-//              lane order, and the group's first lane advances the tile's
-//              running offset for that key.  perm[rowptr + offset + rank] = e.
+//   4. place   one wavefront per tile: running offsets rowptr[n] + offset of
+//              the tile in node n's list start in LDS; the tile's edges are
+//              taken 64 at a time (destinations prefetched 16 steps ahead);
+//              lanes with equal keys are matched with ballots, ranked by lane
+//              order, and the group's first lane advances the key's offset.
+//              perm[offset + rank] = e.
 //
-// Every destination is range-checked; an out-of-range one sets a flag that the
-// host reads back, and is never used as an index.
+// Every destination is range-checked; an out-of-range one is never used as an
+// index and raises the validation flag.
 #include "zs_internal.h"
 
 namespace zs {
@@ -48,16 +52,19 @@ __global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
 template <bool kLds>
 __global__ __launch_bounds__(kCountThreads) void csr_count_kernel(
     const int64_t* __restrict__ dst, int64_t n_edges, int64_t n_nodes, int64_t tile_edges,
-    int32_t* __restrict__ counts, int32_t* __restrict__ flag) {
+    int32_t* __restrict__ counts, int32_t* __restrict__ tile_bad) {
     extern __shared__ int32_t bins[];
     const int64_t t = blockIdx.x;
     const int64_t e0 = t * tile_edges;
     const int64_t e1 = e0 + tile_edges < n_edges ? e0 + tile_edges : n_edges;
     int32_t* row = counts + t * n_nodes;
-    if (kLds) {
-        for (int64_t i = threadIdx.x; i < n_nodes; i += kCountThreads) bins[i] = 0;
-        __syncthreads();
+    for (int64_t i = threadIdx.x; i < n_nodes; i += kCountThreads) {
+        if (kLds)
+            bins[i] = 0;
+        else
+            row[i] = 0;
     }
+    __syncthreads();
     int bad = 0;
     for (int64_t e = e0 + threadIdx.x; e < e1; e += kCountThreads) {
         const int64_t key = dst[e];
@@ -70,27 +77,72 @@ __global__ __launch_bounds__(kCountThreads) void csr_count_kernel(
             bad = 1;
         }
     }
-    if (bad) atomicOr(flag, 1);
-    if (kLds) {
-        __syncthreads();
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) tile_bad[t] = bad;
+    if (kLds)
         for (int64_t i = threadIdx.x; i < n_nodes; i += kCountThreads) row[i] = bins[i];
-    }
 }
 
 // Per node: counts[t][n] <- sum_{t' < t} counts[t'][n]; rowptr[n+1] <- degree.
-__global__ __launch_bounds__(256) void csr_colscan_kernel(int32_t* __restrict__ counts,
-                                                          int64_t tiles, int64_t n_nodes,
-                                                          int32_t* __restrict__ rowptr) {
-    for (int64_t n = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; n < n_nodes;
-         n += int64_t(gridDim.x) * blockDim.x) {
-        int32_t run = 0;
-        for (int64_t t = 0; t < tiles; ++t) {
-            const int32_t c = counts[t * n_nodes + n];
-            counts[t * n_nodes + n] = run;
-            run += c;
+// Workgroup = kColNodes nodes x kColChunks tile chunks.  Block 0 also folds the
+// per-tile validation bits into the flag and sets rowptr[0].
+constexpr int kColNodes = 32;
+constexpr int kColChunks = 8;
+__global__ __launch_bounds__(kColNodes * kColChunks) void csr_colscan_kernel(
+    int32_t* __restrict__ counts, int64_t tiles, int64_t n_nodes, int32_t* __restrict__ rowptr,
+    const int32_t* __restrict__ tile_bad, int32_t* __restrict__ flag) {
+    __shared__ int32_t chunk_sum[kColChunks][kColNodes];
+    const int i = threadIdx.x % kColNodes;
+    const int c = threadIdx.x / kColNodes;
+    const int64_t n = int64_t(blockIdx.x) * kColNodes + i;
+    const int64_t t_lo = tiles * c / kColChunks;
+    const int64_t t_hi = tiles * (c + 1) / kColChunks;
+    int32_t sum = 0;
+    if (n < n_nodes) {
+        int64_t t = t_lo;
+        for (; t + 8 <= t_hi; t += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = counts[(t + u) * n_nodes + n];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sum += v[u];
         }
-        rowptr[n + 1] = run;
-        if (n == 0) rowptr[0] = 0;
+        for (; t < t_hi; ++t) sum += counts[t * n_nodes + n];
+    }
+    chunk_sum[c][i] = sum;
+    __syncthreads();
+    int32_t run = 0, total = 0;
+    for (int cc = 0; cc < kColChunks; ++cc) {
+        if (cc < c) run += chunk_sum[cc][i];
+        total += chunk_sum[cc][i];
+    }
+    if (n < n_nodes) {
+        int64_t t = t_lo;
+        for (; t + 8 <= t_hi; t += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = counts[(t + u) * n_nodes + n];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                counts[(t + u) * n_nodes + n] = run;
+                run += v[u];
+            }
+        }
+        for (; t < t_hi; ++t) {
+            const int32_t v = counts[t * n_nodes + n];
+            counts[t * n_nodes + n] = run;
+            run += v;
+        }
+        if (c == 0) rowptr[n + 1] = total;
+    }
+    if (blockIdx.x == 0) {
+        int bad = 0;
+        for (int64_t t = threadIdx.x; t < tiles; t += blockDim.x) bad |= tile_bad[t];
+        bad = __syncthreads_or(bad);
+        if (threadIdx.x == 0) {
+            *flag = bad ? 1 : 0;
+            rowptr[0] = 0;
+        }
     }
 }
 
@@ -166,6 +218,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_add_kernel(int32_t* __restr
         if (base + i < n) a[base + i] += off;
 }
 
+constexpr int kPlaceAhead = 16;   // 64-edge steps whose destinations are prefetched
+
 template <bool kLds>
 __global__ __launch_bounds__(64) void csr_place_kernel(
     const int64_t* __restrict__ dst, int64_t n_edges, int64_t n_nodes, int64_t tile_edges,
@@ -178,38 +232,49 @@ __global__ __launch_bounds__(64) void csr_place_kernel(
     const int64_t e1 = e0 + tile_edges < n_edges ? e0 + tile_edges : n_edges;
     int32_t* row = counts + t * n_nodes;
     if (kLds) {
-        for (int64_t i = lane; i < n_nodes; i += 64) run[i] = row[i];
+        // running position of the next edge of node n inside this tile
+        for (int64_t i = lane; i < n_nodes; i += 64) run[i] = rowptr[i] + row[i];
         __syncthreads();
     }
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    for (int64_t base = e0; base < e1; base += 64) {
-        const int64_t e = base + lane;
-        const bool in = e < e1;
-        const int64_t key64 = in ? dst[e] : -1;
-        const bool ok = in && key64 >= 0 && key64 < n_nodes;
-        const int32_t key = ok ? int32_t(key64) : 0;
-        if (in) dst32[e] = ok ? key : -1;
-        uint64_t same = __ballot(ok);
-        for (int b = 0; b < key_bits; ++b) {
-            const bool bit = (key >> b) & 1;
-            const uint64_t bal = __ballot(ok && bit);
-            same &= bit ? bal : ~bal;
+    for (int64_t chunk = e0; chunk < e1; chunk += 64 * kPlaceAhead) {
+        int64_t keys[kPlaceAhead];
+#pragma unroll
+        for (int j = 0; j < kPlaceAhead; ++j) {
+            const int64_t e = chunk + j * 64 + lane;
+            keys[j] = e < e1 ? dst[e] : -1;
         }
-        const int rank = __popcll(same & below);
-        const int cnt = __popcll(same);
-        const int leader = ok ? __ffsll((unsigned long long)same) - 1 : lane;
-        int32_t old = 0;
-        if (ok && rank == 0) {
-            if (kLds) {
-                old = run[key];
-                run[key] = old + cnt;
-            } else {
-                old = atomicAdd(&row[key], cnt);
+#pragma unroll
+        for (int j = 0; j < kPlaceAhead; ++j) {
+            const int64_t e = chunk + j * 64 + lane;
+            if (chunk + j * 64 >= e1) break;           // uniform
+            const bool in = e < e1;
+            const int64_t key64 = keys[j];
+            const bool ok = in && key64 >= 0 && key64 < n_nodes;
+            const int32_t key = ok ? int32_t(key64) : 0;
+            if (in) dst32[e] = ok ? key : -1;
+            uint64_t same = __ballot(ok);
+            for (int b = 0; b < key_bits; ++b) {
+                const bool bit = (key >> b) & 1;
+                const uint64_t bal = __ballot(ok && bit);
+                same &= bit ? bal : ~bal;
             }
+            const int rank = __popcll(same & below);
+            const int cnt = __popcll(same);
+            const int leader = ok ? __ffsll((unsigned long long)same) - 1 : lane;
+            int32_t base = 0;
+            if (ok && rank == 0) {
+                if (kLds) {
+                    base = run[key];
+                    run[key] = base + cnt;
+                } else {
+                    base = rowptr[key] + atomicAdd(&row[key], cnt);
+                }
+            }
+            base = __shfl(base, leader, 64);
+            const int64_t pos = int64_t(base) + rank;
+            if (ok && pos >= 0 && pos < n_edges) perm[pos] = int32_t(e);
         }
-        old = __shfl(old, leader, 64);
-        const int64_t pos = int64_t(rowptr[key]) + old + rank;
-        if (ok && pos >= 0 && pos < n_edges) perm[pos] = int32_t(e);
     }
 }
 
@@ -249,7 +314,8 @@ CsrPlan plan_csr(int64_t n_edges, int64_t n_nodes) {
     p.scan_blocks = (n_nodes + kScanBlock - 1) / kScanBlock;
     auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
     p.off_flag = 0;
-    p.off_counts = 256;
+    p.off_tile_bad = 256;
+    p.off_counts = align(p.off_tile_bad + size_t(tiles) * sizeof(int32_t));
     p.off_blocks = align(p.off_counts + size_t(tiles) * size_t(n_nodes) * sizeof(int32_t));
     p.bytes = align(p.off_blocks + size_t(p.scan_blocks > 0 ? p.scan_blocks : 1) * sizeof(int32_t));
     return p;
@@ -260,23 +326,20 @@ hipError_t launch_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int3
                       int32_t* flag, hipStream_t stream) {
     char* ws = static_cast<char*>(workspace);
     if (!flag) flag = reinterpret_cast<int32_t*>(ws + plan.off_flag);
+    int32_t* tile_bad = reinterpret_cast<int32_t*>(ws + plan.off_tile_bad);
     int32_t* counts = reinterpret_cast<int32_t*>(ws + plan.off_counts);
     int32_t* sums = reinterpret_cast<int32_t*>(ws + plan.off_blocks);
     hipError_t err;
-    if ((err = launch_fill_i32(flag, 1, 0, stream)) != hipSuccess) return err;
-    if (!plan.lds_bins &&
-        (err = launch_fill_i32(counts, plan.tiles * n_nodes, 0, stream)) != hipSuccess)
-        return err;
     const size_t lds = plan.lds_bins ? size_t(n_nodes) * sizeof(int32_t) : 0;
     if (plan.lds_bins)
         csr_count_kernel<true><<<unsigned(plan.tiles), kCountThreads, lds, stream>>>(
-            dst, n_edges, n_nodes, plan.tile_edges, counts, flag);
+            dst, n_edges, n_nodes, plan.tile_edges, counts, tile_bad);
     else
         csr_count_kernel<false><<<unsigned(plan.tiles), kCountThreads, 0, stream>>>(
-            dst, n_edges, n_nodes, plan.tile_edges, counts, flag);
+            dst, n_edges, n_nodes, plan.tile_edges, counts, tile_bad);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    csr_colscan_kernel<<<grid_for(n_nodes, 256), 256, 0, stream>>>(counts, plan.tiles, n_nodes,
-                                                                   rowptr);
+    csr_colscan_kernel<<<grid_for(n_nodes, kColNodes, int64_t(1) << 30), kColNodes * kColChunks, 0,
+                         stream>>>(counts, plan.tiles, n_nodes, rowptr, tile_bad, flag);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // inclusive scan of degrees in rowptr[1..N] -> rowptr[n+1] = edges with dst <= n
     scan_block_kernel<<<unsigned(plan.scan_blocks), kScanThreads, 0, stream>>>(rowptr + 1, n_nodes,

@@ -123,6 +123,175 @@ __global__ __launch_bounds__(64) void zs_fwd_kernel(const float* __restrict__ co
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Staged forward for C % 4 == 0 with 16-byte aligned radial and out.
+//
+// Same lane mapping as above with VEC = 4, NQ = 8 (lane = j*8 + q: rows 2j+1,
+// 2j+2 and channels 4q..4q+3 of a 32-channel tile).  The edges of a node are
+// taken 16 at a time (a batch).  A batch's radial rows (16 x 3 x 32 floats)
+// and coupling rows (16 x 15 floats) are fetched with coalesced, all-distinct
+// 16-byte / 4-byte loads (six float4 and up to four floats per lane), kept in
+// registers while the previous batch is being accumulated, then written to
+// LDS from where each lane reads the float4 and two weights it needs per edge.
+// The perm entries of a batch are fetched two batches ahead, so every data
+// load is issued one batch before it is consumed and no load waits on another.
+// Accumulation order and arithmetic are the same as in zs_fwd_kernel.
+// ---------------------------------------------------------------------------
+#ifndef ZS_FWD_BATCH
+#define ZS_FWD_BATCH 8
+#endif
+constexpr int kFwdBatch = ZS_FWD_BATCH;
+constexpr int kFwdRadVec = kFwdBatch * kSlots * 8 / 64;   // float4 per lane per batch (6)
+constexpr int kFwdCplVec = (kFwdBatch * kZonal + 63) / 64; // floats per lane per batch (4)
+
+struct FwdRegs {
+    float4 r[kFwdRadVec];
+    float w[kFwdCplVec];
+};
+
+// Lane mapping of the coalesced batch fetch (i = fetch slot, lane = 0..63):
+//   radial float4 f = i*64 + lane -> batch edge f / 24, slot (f % 24) / 8, quad f % 8
+//   coupling float idx = i*64 + lane -> batch edge idx / 15, column idx % 15 (idx < 240)
+__device__ __attribute__((always_inline)) inline int fwd_rad_edge(int i, int lane) {
+    return (i * 64 + lane) / (kSlots * 8);
+}
+__device__ __attribute__((always_inline)) inline int fwd_rad_rem(int i, int lane) {
+    return (i * 64 + lane) % (kSlots * 8);
+}
+__device__ __attribute__((always_inline)) inline int fwd_cpl_idx(int i, int lane) {
+    return i * 64 + lane;
+}
+
+__device__ __attribute__((always_inline)) inline int fwd_perm_lane(const int32_t* __restrict__ perm, int64_t k, int64_t k1,
+                                    int64_t n_edges, int lane) {
+    int32_t e = -1;
+    if (lane < kFwdBatch && k + lane < k1) {
+        e = perm[k + lane];
+        if (e < 0 || e >= n_edges) e = -1;
+    }
+    return e;
+}
+
+__device__ __attribute__((always_inline)) inline void fwd_fetch(FwdRegs& R, int lane, int pe,
+                                                                 const float* __restrict__ coupling,
+                                                                 const float* __restrict__ radial,
+                                                                 int64_t row_stride, int64_t C,
+                                                                 int64_t cbase) {
+#pragma unroll
+    for (int i = 0; i < kFwdRadVec; ++i) {
+        const int rem = fwd_rad_rem(i, lane);
+        const int64_t ch = cbase + (rem & 7) * 4;
+        const int e = __shfl(pe, fwd_rad_edge(i, lane), 64);
+        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (e >= 0 && ch < C)
+            v = load_stream4<ZS_FWD_NT != 0>(radial + int64_t(e) * row_stride + (rem >> 3) * C + ch);
+        R.r[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < kFwdCplVec; ++i) {
+        const int idx = fwd_cpl_idx(i, lane);
+        const bool in = idx < kFwdBatch * kZonal;
+        const int e = __shfl(pe, in ? idx / kZonal : 0, 64);
+        float v = 0.0f;
+        if (in && e >= 0) v = coupling[int64_t(e) * kZonal + idx % kZonal];
+        R.w[i] = v;
+    }
+}
+
+__device__ __attribute__((always_inline)) inline void fwd_stage_accumulate(
+    const FwdRegs& R, float4* rsh, float* csh, int cnt, int lane, int q, int j, int sA, int sB,
+    float (&acc0)[4], float (&acc1)[4]) {
+#pragma unroll
+    for (int i = 0; i < kFwdRadVec; ++i) rsh[i * 64 + lane] = R.r[i];
+#pragma unroll
+    for (int i = 0; i < kFwdCplVec; ++i) {
+        const int idx = fwd_cpl_idx(i, lane);
+        if (idx < kFwdBatch * kZonal) csh[(idx / kZonal) * 16 + idx % kZonal] = R.w[i];
+    }
+    for (int b = 0; b < cnt; ++b) {
+        const float4 xa = rsh[b * (kSlots * 8) + sA * 8 + q];
+        const float4 xb = rsh[b * (kSlots * 8) + sB * 8 + q];
+        const float w0 = csh[b * 16 + 2 * j];
+        const float w1 = csh[b * 16 + 2 * j + 1];
+        float m;
+        m = w0 * xa.x; acc0[0] = acc0[0] + m;
+        m = w0 * xa.y; acc0[1] = acc0[1] + m;
+        m = w0 * xa.z; acc0[2] = acc0[2] + m;
+        m = w0 * xa.w; acc0[3] = acc0[3] + m;
+        m = w1 * xb.x; acc1[0] = acc1[0] + m;
+        m = w1 * xb.y; acc1[1] = acc1[1] + m;
+        m = w1 * xb.z; acc1[2] = acc1[2] + m;
+        m = w1 * xb.w; acc1[3] = acc1[3] + m;
+    }
+}
+
+__global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restrict__ coupling,
+                                                           const float* __restrict__ radial,
+                                                           const int32_t* __restrict__ rowptr,
+                                                           const int32_t* __restrict__ perm,
+                                                           int64_t n_nodes, int64_t n_edges,
+                                                           int64_t C, float* __restrict__ out) {
+    __shared__ float4 rsh[kFwdBatch * kSlots * 8];
+    __shared__ float csh[kFwdBatch * 16];
+
+    const int lane = threadIdx.x;
+    const int q = lane & 7;
+    const int j = lane >> 3;
+    const int rA = 2 * j + 1;                 // rows rA, rA + 1 (rA + 1 == 16 is row 0)
+    const int sA = row_slot(rA);
+    const int sB = row_slot(rA + 1 <= kZonal ? rA + 1 : kZonal);
+    const int64_t cbase = int64_t(blockIdx.y) * 32;
+    const int64_t c0 = cbase + q * 4;
+    const bool act = c0 < C;
+    const int64_t row_stride = int64_t(kSlots) * C;
+
+    if (lane < kFwdBatch) csh[lane * 16 + 15] = 0.0f;   // pad column, never fetched
+
+    for (int64_t node = blockIdx.x; node < n_nodes; node += gridDim.x) {
+        int64_t k0 = rowptr[node];
+        int64_t k1 = rowptr[node + 1];
+        k0 = k0 < 0 ? 0 : (k0 > n_edges ? n_edges : k0);
+        k1 = k1 < k0 ? k0 : (k1 > n_edges ? n_edges : k1);
+        const int64_t nb = (k1 - k0 + kFwdBatch - 1) / kFwdBatch;
+
+        float acc0[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float acc1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        auto batch_count = [k0, k1](int64_t t) {
+            const int64_t kb = k0 + t * kFwdBatch;
+            return int(k1 - kb < kFwdBatch ? k1 - kb : kFwdBatch);
+        };
+
+        if (nb > 0) {
+            FwdRegs RA, RB;
+            int pA = fwd_perm_lane(perm, k0, k1, n_edges, lane);
+            int pB = fwd_perm_lane(perm, k0 + kFwdBatch, k1, n_edges, lane);
+            fwd_fetch(RA, lane, pA, coupling, radial, row_stride, C, cbase);
+            for (int64_t t = 0; t < nb; t += 2) {
+                pA = fwd_perm_lane(perm, k0 + (t + 2) * kFwdBatch, k1, n_edges, lane);
+                if (t + 1 < nb) fwd_fetch(RB, lane, pB, coupling, radial, row_stride, C, cbase);
+                fwd_stage_accumulate(RA, rsh, csh, batch_count(t), lane, q, j, sA, sB, acc0, acc1);
+                if (t + 1 >= nb) break;
+                pB = fwd_perm_lane(perm, k0 + (t + 3) * kFwdBatch, k1, n_edges, lane);
+                if (t + 2 < nb) fwd_fetch(RA, lane, pA, coupling, radial, row_stride, C, cbase);
+                fwd_stage_accumulate(RB, rsh, csh, batch_count(t + 1), lane, q, j, sA, sB, acc0,
+                                     acc1);
+            }
+        }
+
+        if (act) {
+            float* onode = out + node * kRows * C + c0;
+            *reinterpret_cast<float4*>(onode + int64_t(rA) * C) =
+                make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
+            if (rA + 1 <= kZonal)
+                *reinterpret_cast<float4*>(onode + int64_t(rA + 1) * C) =
+                    make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
+            else
+                *reinterpret_cast<float4*>(onode) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_forward(const float* coupling, const float* radial, const int32_t* rowptr,
@@ -131,10 +300,9 @@ hipError_t launch_forward(const float* coupling, const float* radial, const int3
     constexpr int64_t kGridCap = 1 << 20;
     const unsigned gx = unsigned(n_nodes < kGridCap ? n_nodes : kGridCap);
     if (vec4) {
-        constexpr int NQ = 8, VEC = 4;
-        const unsigned gy = unsigned((channels + NQ * VEC - 1) / (NQ * VEC));
-        zs_fwd_kernel<VEC, NQ, 8><<<dim3(gx, gy), 64, 0, stream>>>(coupling, radial, rowptr, perm,
-                                                                   n_nodes, n_edges, channels, out);
+        const unsigned gy = unsigned((channels + 31) / 32);
+        zs_fwd_staged_kernel<<<dim3(gx, gy), 64, 0, stream>>>(coupling, radial, rowptr, perm,
+                                                              n_nodes, n_edges, channels, out);
     } else {
         constexpr int NQ = 16, VEC = 1;
         const unsigned gy = unsigned((channels + NQ * VEC - 1) / (NQ * VEC));

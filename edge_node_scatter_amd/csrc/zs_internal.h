@@ -38,12 +38,44 @@ struct VecT<1> {
     __device__ static float get(const T& v, int) { return v; }
 };
 
+// Read-once / write-once 16-byte accesses of radial and grad_radial rows.
+// NT = true marks them non-temporal (streamed past the caches), which keeps
+// the L2 and the memory-side cache for the data that is reused (coupling
+// lines shared by neighbouring edges, the upstream rows of a node).
+typedef float zs_f4 __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __attribute__((always_inline)) inline float4 load_stream4(const float* p) {
+    if (NT) {
+        const zs_f4 v = __builtin_nontemporal_load(reinterpret_cast<const zs_f4*>(p));
+        return make_float4(v.x, v.y, v.z, v.w);
+    }
+    return *reinterpret_cast<const float4*>(p);
+}
+template <bool NT>
+__device__ __attribute__((always_inline)) inline void store_stream4(float* p, float4 v) {
+    if (NT) {
+        zs_f4 t = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(t, reinterpret_cast<zs_f4*>(p));
+    } else {
+        *reinterpret_cast<float4*>(p) = v;
+    }
+}
+
+// Build-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef ZS_FWD_NT
+#define ZS_FWD_NT 0
+#endif
+#ifndef ZS_BWD_NT
+#define ZS_BWD_NT 1
+#endif
+
 // ---- CSR build ------------------------------------------------------------
 struct CsrPlan {
     int64_t tiles;        // number of edge tiles (one wavefront each in placement)
     int64_t tile_edges;   // edges per tile (last tile may be shorter)
     bool lds_bins;        // per-tile bins fit in LDS
     size_t off_flag;      // int32 error flag
+    size_t off_tile_bad;  // int32 [tiles] per-tile out-of-range indicator
     size_t off_counts;    // int32 [tiles][n_nodes] per-tile counts, then offsets
     size_t off_blocks;    // int32 scan block sums
     int64_t scan_blocks;
