@@ -197,6 +197,8 @@ __global__ __launch_bounds__(256) void zs_bwd_kernel(
 //    (three per lane) and its coupling rows (EPW x 15 floats, fetched with
 //    coalesced all-distinct loads, at most two per lane) one step ahead into
 //    one of two register buffers, so loads overlap the previous step's math.
+//    Every load is unconditional (absent edges read a valid substitute) so the
+//    compiler can wait for exactly the buffer it consumes.
 //    The coupling floats go through LDS so every lane of an edge gets the
 //    edge's 15 weights.
 //  - The 15 row sums of grad_coupling are reduced in two rounds (rows 1-8 of
@@ -213,17 +215,29 @@ struct BwdRegs {
     float w[CPL];
 };
 
-__device__ __attribute__((always_inline)) inline int bwd_perm(const int32_t* __restrict__ perm,
-                                                              int64_t k, int64_t k1,
-                                                              int64_t n_edges) {
-    int32_t e = -1;
-    if (k < k1) {
-        e = perm[k];
-        if (e < 0 || e >= n_edges) e = -1;
-    }
-    return e;
+// A step's perm entry (lane's edge slot b), fetched one step before it is
+// used.  The load is issued from a valid position (clamped to the node's last
+// edge) and range-checked only when used, so it never forces an early wait.
+struct PermRaw {
+    int32_t raw;
+    bool valid;
+};
+
+__device__ __attribute__((always_inline)) inline PermRaw bwd_perm_issue(
+    const int32_t* __restrict__ perm, int64_t k, int64_t k1) {
+    PermRaw p;
+    p.valid = k < k1;
+    p.raw = perm[p.valid ? k : k1 - 1];
+    return p;
 }
 
+__device__ __attribute__((always_inline)) inline int bwd_perm_resolve(PermRaw p, int64_t n_edges) {
+    return (p.valid && p.raw >= 0 && p.raw < n_edges) ? p.raw : -1;
+}
+
+// Loads of one step, all unconditional: absent edges read edge 0 and channels
+// past C read channel 0; such values are zeroed (channels) or never stored
+// (edges), so they cannot reach a result.
 template <int NQ>
 __device__ __attribute__((always_inline)) inline void bwd_fetch(BwdRegs<NQ>& R, int e, int lane,
                                                                  bool cact, int64_t c0,
@@ -232,22 +246,19 @@ __device__ __attribute__((always_inline)) inline void bwd_fetch(BwdRegs<NQ>& R, 
                                                                  int64_t C) {
     constexpr int EPW = BwdRegs<NQ>::EPW;
     const int64_t row_stride = int64_t(kSlots) * C;
+    const int64_t es = e >= 0 ? e : 0;
+    const int64_t cs = cact ? c0 : 0;
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (e >= 0 && cact)
-            v = load_stream4<ZS_BWD_NT != 0>(radial + int64_t(e) * row_stride + s * C + c0);
-        R.x[s] = v;
-    }
+    for (int s = 0; s < kSlots; ++s)
+        R.x[s] = load_stream4<ZS_BWD_NT != 0>(radial + es * row_stride + s * C + cs);
 #pragma unroll
     for (int i = 0; i < BwdRegs<NQ>::CPL; ++i) {
         const int idx = i * 64 + lane;               // coupling float of this step
         const bool in = idx < EPW * kZonal;
         const int owner = (in ? idx / kZonal : 0) * NQ;   // a lane of that edge slot
         const int ee = __shfl(e, owner, 64);
-        float v = 0.0f;
-        if (in && ee >= 0) v = coupling[int64_t(ee) * kZonal + idx % kZonal];
-        R.w[i] = v;
+        const int64_t ees = ee >= 0 ? ee : 0;
+        R.w[i] = coupling[ees * kZonal + (in ? idx % kZonal : 0)];
     }
 }
 
@@ -307,7 +318,7 @@ __device__ __attribute__((always_inline)) inline double reduce8(double (&v)[8], 
     }
 }
 
-template <int NQ>
+template <int NQ, bool FULL>
 __device__ __attribute__((always_inline)) inline void bwd_compute(
     const BwdRegs<NQ>& R, int e, int lane, int b, bool cact, int64_t c0, int q,
     const float4* gsh, float* wsh, int64_t C, float* __restrict__ grad_coupling,
@@ -328,6 +339,10 @@ __device__ __attribute__((always_inline)) inline void bwd_compute(
     const bool ok = e >= 0;
     const bool act = ok && cact;
     const int64_t row_stride = int64_t(kSlots) * C;
+    float4 x[kSlots];   // lanes past C contribute exact zeros to the channel sums
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s)
+        x[s] = (FULL || cact) ? R.x[s] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float* grow = grad_radial + int64_t(ok ? e : 0) * row_stride + c0;
     float* gcrow = grad_coupling + int64_t(ok ? e : 0) * kZonal;
 #pragma unroll
@@ -352,7 +367,7 @@ __device__ __attribute__((always_inline)) inline void bwd_compute(
             for (int v = 0; v < 4; ++v) {
                 const float p = comp(g, v) * w[r - 1];
                 acc[s][v] = acc[s][v] + p;
-                part[r - r_lo] = __builtin_fma(double(comp(g, v)), double(comp(R.x[s], v)),
+                part[r - r_lo] = __builtin_fma(double(comp(g, v)), double(comp(x[s], v)),
                                                part[r - r_lo]);
             }
         }
@@ -370,18 +385,17 @@ __device__ __attribute__((always_inline)) inline void bwd_compute(
     }
 }
 
-// Occupancy request for the staged backward (build-time tuning knob).
+// Occupancy request for the staged backward: 4 wavefronts per SIMD (<= 128
+// VGPRs) when every lane holds real channels; the masked variants need a few
+// more registers and are left to the compiler (3 per SIMD) rather than spill.
 #ifndef ZS_BWD_WAVES_PER_EU
 #define ZS_BWD_WAVES_PER_EU 4
 #endif
-#if ZS_BWD_WAVES_PER_EU > 0
-#define ZS_BWD_OCCUPANCY __attribute__((amdgpu_waves_per_eu(ZS_BWD_WAVES_PER_EU)))
-#else
-#define ZS_BWD_OCCUPANCY
-#endif
 
-template <int NQ>
-__global__ __launch_bounds__(64) ZS_BWD_OCCUPANCY void zs_bwd_staged_kernel(
+// FULL: C == 4*NQ, every lane holds real channels (no channel masking).
+template <int NQ, bool FULL>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FULL ? ZS_BWD_WAVES_PER_EU : 1)))
+void zs_bwd_staged_kernel(
     const float* __restrict__ grad_out, const float* __restrict__ coupling,
     const float* __restrict__ radial, const int32_t* __restrict__ rowptr,
     const int32_t* __restrict__ perm, int64_t n_nodes, int64_t n_edges, int64_t C,
@@ -394,7 +408,7 @@ __global__ __launch_bounds__(64) ZS_BWD_OCCUPANCY void zs_bwd_staged_kernel(
     const int q = lane % NQ;
     const int b = lane / NQ;
     const int64_t c0 = int64_t(q) * 4;
-    const bool cact = c0 < C;
+    const bool cact = FULL || c0 < C;
     if (lane < EPW) wsh[lane * 16 + 15] = 0.0f;     // pad column, never fetched
 
     for (int64_t node = blockIdx.x; node < n_nodes; node += gridDim.x) {
@@ -413,24 +427,20 @@ __global__ __launch_bounds__(64) ZS_BWD_OCCUPANCY void zs_bwd_staged_kernel(
         }
         const int64_t nsteps = (k1 - k0 + EPW - 1) / EPW;
         BwdRegs<NQ> A, B;
-        int eA = bwd_perm(perm, k0 + b, k1, n_edges);
-        int pB = bwd_perm(perm, k0 + EPW + b, k1, n_edges);
-        int eB = -1;
+        const PermRaw qA = bwd_perm_issue(perm, k0 + b, k1);
+        PermRaw qB = bwd_perm_issue(perm, k0 + EPW + b, k1);
+        int eA = bwd_perm_resolve(qA, n_edges);
         bwd_fetch<NQ>(A, eA, lane, cact, c0, coupling, radial, C);
         for (int64_t t = 0; t < nsteps; t += 2) {
-            const int pN = bwd_perm(perm, k0 + (t + 2) * EPW + b, k1, n_edges);
-            if (t + 1 < nsteps) {
-                bwd_fetch<NQ>(B, pB, lane, cact, c0, coupling, radial, C);
-                eB = pB;
-            }
-            bwd_compute<NQ>(A, eA, lane, b, cact, c0, q, gsh, wsh, C, grad_coupling, grad_radial);
+            const PermRaw qN = bwd_perm_issue(perm, k0 + (t + 2) * EPW + b, k1);
+            const int eB = bwd_perm_resolve(qB, n_edges);
+            bwd_fetch<NQ>(B, eB, lane, cact, c0, coupling, radial, C);
+            bwd_compute<NQ, FULL>(A, eA, lane, b, cact, c0, q, gsh, wsh, C, grad_coupling, grad_radial);
             if (t + 1 >= nsteps) break;
-            pB = bwd_perm(perm, k0 + (t + 3) * EPW + b, k1, n_edges);
-            if (t + 2 < nsteps) {
-                bwd_fetch<NQ>(A, pN, lane, cact, c0, coupling, radial, C);
-                eA = pN;
-            }
-            bwd_compute<NQ>(B, eB, lane, b, cact, c0, q, gsh, wsh, C, grad_coupling, grad_radial);
+            qB = bwd_perm_issue(perm, k0 + (t + 3) * EPW + b, k1);
+            eA = bwd_perm_resolve(qN, n_edges);
+            bwd_fetch<NQ>(A, eA, lane, cact, c0, coupling, radial, C);
+            bwd_compute<NQ, FULL>(B, eB, lane, b, cact, c0, q, gsh, wsh, C, grad_coupling, grad_radial);
         }
     }
 }
@@ -450,14 +460,19 @@ hipError_t launch_backward(const float* grad_out, const float* coupling, const f
                                                          perm, n_nodes, n_edges, channels,       \
                                                          grad_coupling, grad_radial)
     if (vec4) {
-        if (channels <= 32)
-            zs_bwd_staged_kernel<8><<<gx, 64, 0, stream>>>(grad_out, coupling, radial, rowptr,
-                                                           perm, n_nodes, n_edges, channels,
-                                                           grad_coupling, grad_radial);
-        else if (channels <= 64)
-            zs_bwd_staged_kernel<16><<<gx, 64, 0, stream>>>(grad_out, coupling, radial, rowptr,
-                                                            perm, n_nodes, n_edges, channels,
-                                                            grad_coupling, grad_radial);
+#define ZS_BWD_STAGED(NQ, FULL)                                                                  \
+    zs_bwd_staged_kernel<NQ, FULL><<<gx, 64, 0, stream>>>(grad_out, coupling, radial, rowptr, perm, \
+                                                         n_nodes, n_edges, channels,             \
+                                                         grad_coupling, grad_radial)
+        if (channels == 32)
+            ZS_BWD_STAGED(8, true);
+        else if (channels < 32)
+            ZS_BWD_STAGED(8, false);
+        else if (channels == 64)
+            ZS_BWD_STAGED(16, true);
+        else if (channels < 64)
+            ZS_BWD_STAGED(16, false);
+#undef ZS_BWD_STAGED
         else
             ZS_BWD_LAUNCH(4, 16, false);
     } else {

@@ -232,8 +232,20 @@ __global__ __launch_bounds__(64) void csr_place_kernel(
     const int64_t e1 = e0 + tile_edges < n_edges ? e0 + tile_edges : n_edges;
     int32_t* row = counts + t * n_nodes;
     if (kLds) {
-        // running position of the next edge of node n inside this tile
-        for (int64_t i = lane; i < n_nodes; i += 64) run[i] = rowptr[i] + row[i];
+        // running position of the next edge of node n inside this tile; the
+        // loads of 8 strides are issued before any is consumed
+        int64_t i0 = 0;
+        for (; i0 + 8 * 64 <= n_nodes; i0 += 8 * 64) {
+            int32_t a[8], c[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                a[u] = rowptr[i0 + u * 64 + lane];
+                c[u] = row[i0 + u * 64 + lane];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) run[i0 + u * 64 + lane] = a[u] + c[u];
+        }
+        for (int64_t i = i0 + lane; i < n_nodes; i += 64) run[i] = rowptr[i] + row[i];
         __syncthreads();
     }
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));

@@ -134,8 +134,9 @@ __global__ __launch_bounds__(64) void zs_fwd_kernel(const float* __restrict__ co
 // 16-byte / 4-byte loads (six float4 and up to four floats per lane), kept in
 // registers while the previous batch is being accumulated, then written to
 // LDS from where each lane reads the float4 and two weights it needs per edge.
-// The perm entries of a batch are fetched two batches ahead, so every data
-// load is issued one batch before it is consumed and no load waits on another.
+// The perm entries of a batch are fetched two batches ahead and every load is
+// unconditional (absent edges read a valid substitute), so each data load is
+// issued one batch before it is consumed and no load waits on another.
 // Accumulation order and arithmetic are the same as in zs_fwd_kernel.
 // ---------------------------------------------------------------------------
 #ifndef ZS_FWD_BATCH
@@ -163,16 +164,30 @@ __device__ __attribute__((always_inline)) inline int fwd_cpl_idx(int i, int lane
     return i * 64 + lane;
 }
 
-__device__ __attribute__((always_inline)) inline int fwd_perm_lane(const int32_t* __restrict__ perm, int64_t k, int64_t k1,
-                                    int64_t n_edges, int lane) {
-    int32_t e = -1;
-    if (lane < kFwdBatch && k + lane < k1) {
-        e = perm[k + lane];
-        if (e < 0 || e >= n_edges) e = -1;
-    }
-    return e;
+// A batch's perm entries, fetched one batch before they are used.  Every lane
+// issues its load from a valid position (clamped to the node's last edge) and
+// the entry is range-checked only when it is used, so the load never forces an
+// early wait.  Lane L < span carries the entry of edge k + L.
+struct PermRaw {
+    int32_t raw;
+    bool valid;
+};
+
+__device__ __attribute__((always_inline)) inline PermRaw perm_issue(
+    const int32_t* __restrict__ perm, int64_t k, int64_t k1, int lane, int span) {
+    const int64_t kk = k + lane;
+    PermRaw p;
+    p.valid = lane < span && kk < k1;
+    p.raw = perm[p.valid ? kk : k1 - 1];
+    return p;
 }
 
+__device__ __attribute__((always_inline)) inline int perm_resolve(PermRaw p, int64_t n_edges) {
+    return (p.valid && p.raw >= 0 && p.raw < n_edges) ? p.raw : -1;
+}
+
+// Loads of one batch, all unconditional: absent edges and channels past C read
+// a valid substitute (edge 0, the tile's first channel) that is never used.
 __device__ __attribute__((always_inline)) inline void fwd_fetch(FwdRegs& R, int lane, int pe,
                                                                  const float* __restrict__ coupling,
                                                                  const float* __restrict__ radial,
@@ -183,19 +198,17 @@ __device__ __attribute__((always_inline)) inline void fwd_fetch(FwdRegs& R, int 
         const int rem = fwd_rad_rem(i, lane);
         const int64_t ch = cbase + (rem & 7) * 4;
         const int e = __shfl(pe, fwd_rad_edge(i, lane), 64);
-        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (e >= 0 && ch < C)
-            v = load_stream4<ZS_FWD_NT != 0>(radial + int64_t(e) * row_stride + (rem >> 3) * C + ch);
-        R.r[i] = v;
+        const int64_t es = e >= 0 ? e : 0;
+        const int64_t cs = ch < C ? ch : cbase;
+        R.r[i] = load_stream4<ZS_FWD_NT != 0>(radial + es * row_stride + (rem >> 3) * C + cs);
     }
 #pragma unroll
     for (int i = 0; i < kFwdCplVec; ++i) {
         const int idx = fwd_cpl_idx(i, lane);
         const bool in = idx < kFwdBatch * kZonal;
         const int e = __shfl(pe, in ? idx / kZonal : 0, 64);
-        float v = 0.0f;
-        if (in && e >= 0) v = coupling[int64_t(e) * kZonal + idx % kZonal];
-        R.w[i] = v;
+        const int64_t es = e >= 0 ? e : 0;
+        R.w[i] = coupling[es * kZonal + (in ? idx % kZonal : 0)];
     }
 }
 
@@ -209,7 +222,7 @@ __device__ __attribute__((always_inline)) inline void fwd_stage_accumulate(
         const int idx = fwd_cpl_idx(i, lane);
         if (idx < kFwdBatch * kZonal) csh[(idx / kZonal) * 16 + idx % kZonal] = R.w[i];
     }
-    for (int b = 0; b < cnt; ++b) {
+    auto edge = [&](int b) {
         const float4 xa = rsh[b * (kSlots * 8) + sA * 8 + q];
         const float4 xb = rsh[b * (kSlots * 8) + sB * 8 + q];
         const float w0 = csh[b * 16 + 2 * j];
@@ -223,6 +236,13 @@ __device__ __attribute__((always_inline)) inline void fwd_stage_accumulate(
         m = w1 * xb.y; acc1[1] = acc1[1] + m;
         m = w1 * xb.z; acc1[2] = acc1[2] + m;
         m = w1 * xb.w; acc1[3] = acc1[3] + m;
+    };
+    if (cnt == kFwdBatch) {
+        // full batch: unrolled so the LDS reads of all its edges are in flight
+#pragma unroll
+        for (int b = 0; b < kFwdBatch; ++b) edge(b);
+    } else {
+        for (int b = 0; b < cnt; ++b) edge(b);
     }
 }
 
@@ -264,16 +284,18 @@ __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restri
 
         if (nb > 0) {
             FwdRegs RA, RB;
-            int pA = fwd_perm_lane(perm, k0, k1, n_edges, lane);
-            int pB = fwd_perm_lane(perm, k0 + kFwdBatch, k1, n_edges, lane);
-            fwd_fetch(RA, lane, pA, coupling, radial, row_stride, C, cbase);
+            PermRaw rA = perm_issue(perm, k0, k1, lane, kFwdBatch);
+            PermRaw rB = perm_issue(perm, k0 + kFwdBatch, k1, lane, kFwdBatch);
+            fwd_fetch(RA, lane, perm_resolve(rA, n_edges), coupling, radial, row_stride, C, cbase);
             for (int64_t t = 0; t < nb; t += 2) {
-                pA = fwd_perm_lane(perm, k0 + (t + 2) * kFwdBatch, k1, n_edges, lane);
-                if (t + 1 < nb) fwd_fetch(RB, lane, pB, coupling, radial, row_stride, C, cbase);
+                const PermRaw rN = perm_issue(perm, k0 + (t + 2) * kFwdBatch, k1, lane, kFwdBatch);
+                fwd_fetch(RB, lane, perm_resolve(rB, n_edges), coupling, radial, row_stride, C,
+                          cbase);
                 fwd_stage_accumulate(RA, rsh, csh, batch_count(t), lane, q, j, sA, sB, acc0, acc1);
                 if (t + 1 >= nb) break;
-                pB = fwd_perm_lane(perm, k0 + (t + 3) * kFwdBatch, k1, n_edges, lane);
-                if (t + 2 < nb) fwd_fetch(RA, lane, pA, coupling, radial, row_stride, C, cbase);
+                rB = perm_issue(perm, k0 + (t + 3) * kFwdBatch, k1, lane, kFwdBatch);
+                fwd_fetch(RA, lane, perm_resolve(rN, n_edges), coupling, radial, row_stride, C,
+                          cbase);
                 fwd_stage_accumulate(RB, rsh, csh, batch_count(t + 1), lane, q, j, sA, sB, acc0,
                                      acc1);
             }

@@ -63,7 +63,7 @@ __device__ __attribute__((always_inline)) inline void store_stream4(float* p, fl
 
 // Build-time tuning knobs (defaults are the measured best on MI355X).
 #ifndef ZS_FWD_NT
-#define ZS_FWD_NT 0
+#define ZS_FWD_NT 1
 #endif
 #ifndef ZS_BWD_NT
 #define ZS_BWD_NT 1
