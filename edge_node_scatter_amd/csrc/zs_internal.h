@@ -76,6 +76,7 @@ struct CsrPlan {
     bool lds_bins;        // per-tile bins fit in LDS
     size_t off_flag;      // int32 error flag
     size_t off_tile_bad;  // int32 [tiles] per-tile out-of-range indicator
+    size_t off_deg;       // int32 [n_nodes] degrees
     size_t off_counts;    // int32 [tiles][n_nodes] per-tile counts, then offsets
     size_t off_blocks;    // int32 scan block sums
     int64_t scan_blocks;
