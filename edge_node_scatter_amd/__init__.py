@@ -13,8 +13,10 @@ Functions carry the C ABI's names:
 
 plus ``gie_zonal_scatter(coupling, radial, csr)``, an autograd function with
 the operator boundary of deepmd-kit PR #6072 ("fused Triton zonal scatter for
-the GIE head", section "Boundary and layout contract"): inputs are made
-contiguous first, only fp32 is accepted, and no double backward is provided.
+the GIE head", section "Boundary and layout contract"): only fp32 is
+accepted and no double backward is provided.  Unlike that boundary, strided
+views of the edge inputs are read in place instead of being copied to
+contiguous tensors (``zs_forward_strided`` / ``zs_backward_strided``).
 """
 from __future__ import annotations
 
@@ -62,6 +64,11 @@ def load() -> ctypes.CDLL:
         lib.zs_forward.restype = INT
         lib.zs_backward.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, P, P]
         lib.zs_backward.restype = INT
+        lib.zs_forward_strided.argtypes = [P, I64, P, I64, I64, P, P, I64, I64, I64, P, P]
+        lib.zs_forward_strided.restype = INT
+        lib.zs_backward_strided.argtypes = [P, P, I64, P, I64, I64, P, P, P, I64, I64, I64, P, P,
+                                            P]
+        lib.zs_backward_strided.restype = INT
         _lib = lib
     return _lib
 
@@ -89,12 +96,44 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def _dev_tensor(t: torch.Tensor, name: str, dtype: torch.dtype) -> torch.Tensor:
+def _dev_tensor(t: torch.Tensor, name: str, dtype: torch.dtype,
+                contiguous: bool = True) -> torch.Tensor:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    return t.contiguous()
+    return t.contiguous() if contiguous else t
+
+
+def _edge_views(coupling: torch.Tensor, radial: torch.Tensor):
+    """Coupling (E,15) and radial (E,3,C) as views the strided entry points
+    accept (unit-stride columns / channels, non-negative strides); anything
+    else is copied to a contiguous tensor.  Returns the tensors and their
+    (coupling edge, radial edge, radial slot) strides in floats."""
+    if coupling.dim() != 2 or coupling.shape[1] != ZONAL:
+        raise ValueError("coupling must be (E, 15)")
+    if radial.dim() != 3 or radial.shape[1] != SLOTS or radial.shape[0] != coupling.shape[0]:
+        raise ValueError("radial must be (E, 3, C) with the same E as coupling")
+    if coupling.stride(1) != 1 or coupling.stride(0) < 0:
+        coupling = coupling.contiguous()
+    if radial.stride(2) != 1 or radial.stride(0) < 0 or radial.stride(1) < 0:
+        radial = radial.contiguous()
+    return coupling, radial, (coupling.stride(0), radial.stride(0), radial.stride(1))
+
+
+def coupling_from_band(band: torch.Tensor, m0_offset: int = 15) -> torch.Tensor:
+    """The zonal coupling (E, 15) as a view of a packed (E, 46) Wigner band.
+
+    The band stores, per edge, three segments (the band page's "three
+    structural rows per degree block"): two of 15 entries and the m = 0
+    segment of 16 entries (rows 0..15, row 0 being the l = 0 block).  The
+    pages do not print the segment order; the default m0_offset = 15 reads
+    them in increasing m (m = -1, 0, +1), so the coupling of rows 1..15 is
+    band[:, 16:31].  The view is passed to the kernels without a copy.
+    """
+    if band.dim() != 2 or band.shape[1] != 3 * ROWS - 2:
+        raise ValueError("band must be (E, 46)")
+    return band[:, m0_offset + 1:m0_offset + 1 + ZONAL]
 
 
 class Csr(NamedTuple):
@@ -135,28 +174,34 @@ def zs_build_csr(dst: torch.Tensor, n_nodes: int, workspace: torch.Tensor | None
 
 def zs_forward(coupling: torch.Tensor, radial: torch.Tensor, csr: Csr,
                out: torch.Tensor | None = None) -> torch.Tensor:
-    """out (N, 16, C) fp32 with out[:, 0] = 0."""
-    coupling = _dev_tensor(coupling, "coupling", torch.float32)
-    radial = _dev_tensor(radial, "radial", torch.float32)
-    E = coupling.shape[0]
-    if coupling.shape != (E, ZONAL) or radial.dim() != 3 or radial.shape[:2] != (E, SLOTS):
-        raise ValueError("coupling must be (E, 15) and radial (E, 3, C)")
-    C = radial.shape[2]
+    """out (N, 16, C) fp32 with out[:, 0] = 0.  coupling and radial may be
+    strided views (unit-stride last dimension); they are not copied."""
+    coupling = _dev_tensor(coupling, "coupling", torch.float32, contiguous=False)
+    radial = _dev_tensor(radial, "radial", torch.float32, contiguous=False)
+    coupling, radial, (cs, re, rs) = _edge_views(coupling, radial)
+    E, C = radial.shape[0], radial.shape[2]
     if out is None:
         out = torch.empty((csr.n_nodes, ROWS, C), dtype=torch.float32, device=coupling.device)
-    _check("zs_forward", load().zs_forward(
-        _ptr(coupling), _ptr(radial), _ptr(csr.rowptr), _ptr(csr.perm), csr.n_nodes, E, C,
-        _ptr(out), _stream()))
+    if coupling.is_contiguous() and radial.is_contiguous():
+        status = load().zs_forward(_ptr(coupling), _ptr(radial), _ptr(csr.rowptr), _ptr(csr.perm),
+                                   csr.n_nodes, E, C, _ptr(out), _stream())
+    else:
+        status = load().zs_forward_strided(_ptr(coupling), cs, _ptr(radial), re, rs,
+                                           _ptr(csr.rowptr), _ptr(csr.perm), csr.n_nodes, E, C,
+                                           _ptr(out), _stream())
+    _check("zs_forward", status)
     return out
 
 
 def zs_backward(grad_out: torch.Tensor, coupling: torch.Tensor, radial: torch.Tensor, csr: Csr,
                 grad_coupling: torch.Tensor | None = None,
                 grad_radial: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
-    """(grad_coupling (E, 15), grad_radial (E, 3, C)) fp32."""
+    """(grad_coupling (E, 15), grad_radial (E, 3, C)) fp32, contiguous.
+    coupling and radial may be strided views as in zs_forward."""
     grad_out = _dev_tensor(grad_out, "grad_out", torch.float32)
-    coupling = _dev_tensor(coupling, "coupling", torch.float32)
-    radial = _dev_tensor(radial, "radial", torch.float32)
+    coupling = _dev_tensor(coupling, "coupling", torch.float32, contiguous=False)
+    radial = _dev_tensor(radial, "radial", torch.float32, contiguous=False)
+    coupling, radial, (cs, re, rs) = _edge_views(coupling, radial)
     E, C = radial.shape[0], radial.shape[2]
     if grad_out.shape != (csr.n_nodes, ROWS, C):
         raise ValueError("grad_out must be (N, 16, C)")
@@ -164,9 +209,16 @@ def zs_backward(grad_out: torch.Tensor, coupling: torch.Tensor, radial: torch.Te
         grad_coupling = torch.empty((E, ZONAL), dtype=torch.float32, device=radial.device)
     if grad_radial is None:
         grad_radial = torch.empty((E, SLOTS, C), dtype=torch.float32, device=radial.device)
-    _check("zs_backward", load().zs_backward(
-        _ptr(grad_out), _ptr(coupling), _ptr(radial), _ptr(csr.dst32), _ptr(csr.rowptr),
-        _ptr(csr.perm), csr.n_nodes, E, C, _ptr(grad_coupling), _ptr(grad_radial), _stream()))
+    if coupling.is_contiguous() and radial.is_contiguous():
+        status = load().zs_backward(_ptr(grad_out), _ptr(coupling), _ptr(radial), _ptr(csr.dst32),
+                                    _ptr(csr.rowptr), _ptr(csr.perm), csr.n_nodes, E, C,
+                                    _ptr(grad_coupling), _ptr(grad_radial), _stream())
+    else:
+        status = load().zs_backward_strided(_ptr(grad_out), _ptr(coupling), cs, _ptr(radial), re,
+                                            rs, _ptr(csr.dst32), _ptr(csr.rowptr), _ptr(csr.perm),
+                                            csr.n_nodes, E, C, _ptr(grad_coupling),
+                                            _ptr(grad_radial), _stream())
+    _check("zs_backward", status)
     return grad_coupling, grad_radial
 
 
@@ -188,6 +240,7 @@ class _GieZonalScatter(torch.autograd.Function):
 
 
 def gie_zonal_scatter(coupling: torch.Tensor, radial: torch.Tensor, csr: Csr) -> torch.Tensor:
-    """Differentiable zonal scatter; inputs are made contiguous first."""
-    return _GieZonalScatter.apply(coupling.contiguous(), radial.contiguous(), csr.rowptr,
-                                  csr.perm, csr.dst32, csr.n_nodes)
+    """Differentiable zonal scatter.  Strided views of coupling and radial (for
+    example sliced radial features, or the coupling inside a packed Wigner
+    band) are read in place; the gradients are contiguous tensors."""
+    return _GieZonalScatter.apply(coupling, radial, csr.rowptr, csr.perm, csr.dst32, csr.n_nodes)

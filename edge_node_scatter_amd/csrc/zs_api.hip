@@ -94,30 +94,48 @@ int zs_build_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* 
     return flag ? ZS_ERR_INDEX : ZS_OK;
 }
 
-int zs_forward(const float* coupling, const float* radial, const int32_t* rowptr,
-               const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels, float* out,
-               void* stream) {
+namespace {
+
+// Strided input layouts: any non-negative strides (inputs are only read, so
+// overlapping or broadcast rows are harmless).
+bool layout_ok(int64_t cs, int64_t re, int64_t rs, int64_t C) {
+    (void)C;
+    return cs >= 0 && re >= 0 && rs >= 0;
+}
+
+// Floats spanned by E edges of the strided inputs.
+int64_t cpl_extent(int64_t E, int64_t cs) { return E > 0 ? (E - 1) * cs + zs::kZonal : 0; }
+int64_t rad_extent(int64_t E, int64_t re, int64_t rs, int64_t C) {
+    return E > 0 ? (E - 1) * re + 2 * rs + C : 0;
+}
+
+int forward_impl(const float* coupling, int64_t cs, const float* radial, int64_t re, int64_t rs,
+                 const int32_t* rowptr, const int32_t* perm, int64_t n_nodes, int64_t n_edges,
+                 int64_t channels, float* out, void* stream) {
     if (!sizes_ok(n_edges, n_nodes) || !channels_ok(channels)) return ZS_ERR_SHAPE;
+    if (!layout_ok(cs, re, rs, channels)) return ZS_ERR_SHAPE;
     if (!out || !rowptr || (n_edges > 0 && (!coupling || !radial || !perm))) return ZS_ERR_NULL;
     if (!aligned(out, 4) || !aligned(rowptr, 4) ||
         (n_edges > 0 && (!aligned(coupling, 4) || !aligned(radial, 4) || !aligned(perm, 4))))
         return ZS_ERR_UNSUPPORTED;
     const Range r_out = span(out, n_nodes * zs::kRows * channels, 4);
-    if (overlap(r_out, span(coupling, n_edges * zs::kZonal, 4)) ||
-        overlap(r_out, span(radial, n_edges * zs::kSlots * channels, 4)) ||
+    if (overlap(r_out, span(coupling, cpl_extent(n_edges, cs), 4)) ||
+        overlap(r_out, span(radial, rad_extent(n_edges, re, rs, channels), 4)) ||
         overlap(r_out, span(rowptr, n_nodes + 1, 4)) || overlap(r_out, span(perm, n_edges, 4)))
         return ZS_ERR_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool vec4 = channels % 4 == 0 && aligned(out, 16) && (n_edges == 0 || aligned(radial, 16));
-    return hip_status(zs::launch_forward(coupling, radial, rowptr, perm, n_nodes, n_edges, channels,
-                                         out, vec4, s));
+    const bool vec4 = channels % 4 == 0 && aligned(out, 16) &&
+                      (n_edges == 0 || (aligned(radial, 16) && re % 4 == 0 && rs % 4 == 0));
+    return hip_status(zs::launch_forward(coupling, radial, zs::InLayout{cs, re, rs}, rowptr, perm,
+                                         n_nodes, n_edges, channels, out, vec4, s));
 }
 
-int zs_backward(const float* grad_out, const float* coupling, const float* radial,
-                const int32_t* dst32, const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
-                int64_t n_edges, int64_t channels, float* grad_coupling, float* grad_radial,
-                void* stream) {
+int backward_impl(const float* grad_out, const float* coupling, int64_t cs, const float* radial,
+                  int64_t re, int64_t rs, const int32_t* dst32, const int32_t* rowptr,
+                  const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels,
+                  float* grad_coupling, float* grad_radial, void* stream) {
     if (!sizes_ok(n_edges, n_nodes) || !channels_ok(channels)) return ZS_ERR_SHAPE;
+    if (!layout_ok(cs, re, rs, channels)) return ZS_ERR_SHAPE;
     if (n_edges == 0) return ZS_OK;   // both gradients are empty
     if (!grad_out || !coupling || !radial || !dst32 || !rowptr || !perm || !grad_coupling ||
         !grad_radial)
@@ -129,8 +147,8 @@ int zs_backward(const float* grad_out, const float* coupling, const float* radia
     const Range r_gc = span(grad_coupling, n_edges * zs::kZonal, 4);
     const Range r_gr = span(grad_radial, n_edges * zs::kSlots * channels, 4);
     const Range ins[] = {span(grad_out, n_nodes * zs::kRows * channels, 4),
-                         span(coupling, n_edges * zs::kZonal, 4),
-                         span(radial, n_edges * zs::kSlots * channels, 4),
+                         span(coupling, cpl_extent(n_edges, cs), 4),
+                         span(radial, rad_extent(n_edges, re, rs, channels), 4),
                          span(dst32, n_edges, 4), span(rowptr, n_nodes + 1, 4),
                          span(perm, n_edges, 4)};
     if (overlap(r_gc, r_gr)) return ZS_ERR_ALIAS;
@@ -138,9 +156,47 @@ int zs_backward(const float* grad_out, const float* coupling, const float* radia
         if (overlap(r_gc, in) || overlap(r_gr, in)) return ZS_ERR_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool vec4 = channels % 4 == 0 && aligned(grad_out, 16) && aligned(radial, 16) &&
-                      aligned(grad_radial, 16);
-    return hip_status(zs::launch_backward(grad_out, coupling, radial, dst32, rowptr, perm, n_nodes,
-                                          n_edges, channels, grad_coupling, grad_radial, vec4, s));
+                      aligned(grad_radial, 16) && re % 4 == 0 && rs % 4 == 0;
+    return hip_status(zs::launch_backward(grad_out, coupling, radial, zs::InLayout{cs, re, rs},
+                                          dst32, rowptr, perm, n_nodes, n_edges, channels,
+                                          grad_coupling, grad_radial, vec4, s));
+}
+
+}  // namespace
+
+int zs_forward(const float* coupling, const float* radial, const int32_t* rowptr,
+               const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels, float* out,
+               void* stream) {
+    return forward_impl(coupling, zs::kZonal, radial, zs::kSlots * channels, channels, rowptr,
+                        perm, n_nodes, n_edges, channels, out, stream);
+}
+
+int zs_forward_strided(const float* coupling, int64_t coupling_edge_stride, const float* radial,
+                       int64_t radial_edge_stride, int64_t radial_slot_stride,
+                       const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
+                       int64_t n_edges, int64_t channels, float* out, void* stream) {
+    return forward_impl(coupling, coupling_edge_stride, radial, radial_edge_stride,
+                        radial_slot_stride, rowptr, perm, n_nodes, n_edges, channels, out, stream);
+}
+
+int zs_backward(const float* grad_out, const float* coupling, const float* radial,
+                const int32_t* dst32, const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
+                int64_t n_edges, int64_t channels, float* grad_coupling, float* grad_radial,
+                void* stream) {
+    return backward_impl(grad_out, coupling, zs::kZonal, radial, zs::kSlots * channels, channels,
+                         dst32, rowptr, perm, n_nodes, n_edges, channels, grad_coupling,
+                         grad_radial, stream);
+}
+
+int zs_backward_strided(const float* grad_out, const float* coupling,
+                        int64_t coupling_edge_stride, const float* radial,
+                        int64_t radial_edge_stride, int64_t radial_slot_stride,
+                        const int32_t* dst32, const int32_t* rowptr, const int32_t* perm,
+                        int64_t n_nodes, int64_t n_edges, int64_t channels, float* grad_coupling,
+                        float* grad_radial, void* stream) {
+    return backward_impl(grad_out, coupling, coupling_edge_stride, radial, radial_edge_stride,
+                         radial_slot_stride, dst32, rowptr, perm, n_nodes, n_edges, channels,
+                         grad_coupling, grad_radial, stream);
 }
 
 }  // extern "C"

@@ -63,7 +63,7 @@ __device__ inline int reduce_rows(double (&v)[16], int q) {
 template <int VEC, int NQ, bool GREG>
 __global__ __launch_bounds__(256) void zs_bwd_kernel(
     const float* __restrict__ grad_out, const float* __restrict__ coupling,
-    const float* __restrict__ radial, const int32_t* __restrict__ rowptr,
+    const float* __restrict__ radial, InLayout L, const int32_t* __restrict__ rowptr,
     const int32_t* __restrict__ perm, int64_t n_nodes, int64_t n_edges, int64_t C,
     float* __restrict__ grad_coupling, float* __restrict__ grad_radial) {
     using V = VecT<VEC>;
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void zs_bwd_kernel(
             if (!ok) e = 0;
 
             float w[kZonal];
-            const float* crow = coupling + int64_t(e) * kZonal;
+            const float* crow = coupling + int64_t(e) * L.cpl_edge;
 #pragma unroll
             for (int i = 0; i < kZonal; ++i) w[i] = ok ? crow[i] : 0.0f;
 
@@ -135,11 +135,11 @@ __global__ __launch_bounds__(256) void zs_bwd_kernel(
                     }
                 }
                 float x[kSlots][VEC];
-                const float* rrow = radial + int64_t(e) * row_stride + c0;
+                const float* rrow = radial + int64_t(e) * L.rad_edge + c0;
 #pragma unroll
                 for (int s = 0; s < kSlots; ++s) {
                     VT tv{};
-                    if (act) tv = V::load(rrow + s * C);
+                    if (act) tv = V::load(rrow + s * L.rad_slot);
 #pragma unroll
                     for (int v = 0; v < VEC; ++v) x[s][v] = act ? V::get(tv, v) : 0.0f;
                 }
@@ -243,14 +243,13 @@ __device__ __attribute__((always_inline)) inline void bwd_fetch(BwdRegs<NQ>& R, 
                                                                  bool cact, int64_t c0,
                                                                  const float* __restrict__ coupling,
                                                                  const float* __restrict__ radial,
-                                                                 int64_t C) {
+                                                                 const InLayout& L) {
     constexpr int EPW = BwdRegs<NQ>::EPW;
-    const int64_t row_stride = int64_t(kSlots) * C;
     const int64_t es = e >= 0 ? e : 0;
     const int64_t cs = cact ? c0 : 0;
 #pragma unroll
     for (int s = 0; s < kSlots; ++s)
-        R.x[s] = load_stream4<ZS_BWD_NT != 0>(radial + es * row_stride + s * C + cs);
+        R.x[s] = load_stream4<ZS_BWD_NT != 0>(radial + es * L.rad_edge + s * L.rad_slot + cs);
 #pragma unroll
     for (int i = 0; i < BwdRegs<NQ>::CPL; ++i) {
         const int idx = i * 64 + lane;               // coupling float of this step
@@ -258,7 +257,7 @@ __device__ __attribute__((always_inline)) inline void bwd_fetch(BwdRegs<NQ>& R, 
         const int owner = (in ? idx / kZonal : 0) * NQ;   // a lane of that edge slot
         const int ee = __shfl(e, owner, 64);
         const int64_t ees = ee >= 0 ? ee : 0;
-        R.w[i] = coupling[ees * kZonal + (in ? idx % kZonal : 0)];
+        R.w[i] = coupling[ees * L.cpl_edge + (in ? idx % kZonal : 0)];
     }
 }
 
@@ -397,7 +396,7 @@ template <int NQ, bool FULL>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FULL ? ZS_BWD_WAVES_PER_EU : 1)))
 void zs_bwd_staged_kernel(
     const float* __restrict__ grad_out, const float* __restrict__ coupling,
-    const float* __restrict__ radial, const int32_t* __restrict__ rowptr,
+    const float* __restrict__ radial, InLayout L, const int32_t* __restrict__ rowptr,
     const int32_t* __restrict__ perm, int64_t n_nodes, int64_t n_edges, int64_t C,
     float* __restrict__ grad_coupling, float* __restrict__ grad_radial) {
     constexpr int EPW = 64 / NQ;
@@ -430,16 +429,16 @@ void zs_bwd_staged_kernel(
         const PermRaw qA = bwd_perm_issue(perm, k0 + b, k1);
         PermRaw qB = bwd_perm_issue(perm, k0 + EPW + b, k1);
         int eA = bwd_perm_resolve(qA, n_edges);
-        bwd_fetch<NQ>(A, eA, lane, cact, c0, coupling, radial, C);
+        bwd_fetch<NQ>(A, eA, lane, cact, c0, coupling, radial, L);
         for (int64_t t = 0; t < nsteps; t += 2) {
             const PermRaw qN = bwd_perm_issue(perm, k0 + (t + 2) * EPW + b, k1);
             const int eB = bwd_perm_resolve(qB, n_edges);
-            bwd_fetch<NQ>(B, eB, lane, cact, c0, coupling, radial, C);
+            bwd_fetch<NQ>(B, eB, lane, cact, c0, coupling, radial, L);
             bwd_compute<NQ, FULL>(A, eA, lane, b, cact, c0, q, gsh, wsh, C, grad_coupling, grad_radial);
             if (t + 1 >= nsteps) break;
             qB = bwd_perm_issue(perm, k0 + (t + 3) * EPW + b, k1);
             eA = bwd_perm_resolve(qN, n_edges);
-            bwd_fetch<NQ>(A, eA, lane, cact, c0, coupling, radial, C);
+            bwd_fetch<NQ>(A, eA, lane, cact, c0, coupling, radial, L);
             bwd_compute<NQ, FULL>(B, eB, lane, b, cact, c0, q, gsh, wsh, C, grad_coupling, grad_radial);
         }
     }
@@ -448,22 +447,22 @@ void zs_bwd_staged_kernel(
 }  // namespace
 
 hipError_t launch_backward(const float* grad_out, const float* coupling, const float* radial,
-                           const int32_t* dst32, const int32_t* rowptr, const int32_t* perm,
-                           int64_t n_nodes, int64_t n_edges, int64_t channels,
-                           float* grad_coupling, float* grad_radial, bool vec4,
+                           InLayout L, const int32_t* dst32, const int32_t* rowptr,
+                           const int32_t* perm, int64_t n_nodes, int64_t n_edges,
+                           int64_t channels, float* grad_coupling, float* grad_radial, bool vec4,
                            hipStream_t stream) {
     (void)dst32;   // this traversal is CSR-major; dst32 serves edge-major variants
     constexpr int64_t kGridCap = 1 << 20;
     const unsigned gx = unsigned(n_nodes < kGridCap ? n_nodes : kGridCap);
 #define ZS_BWD_LAUNCH(VEC, NQ, GREG)                                                            \
-    zs_bwd_kernel<VEC, NQ, GREG><<<gx, 256, 0, stream>>>(grad_out, coupling, radial, rowptr,     \
+    zs_bwd_kernel<VEC, NQ, GREG><<<gx, 256, 0, stream>>>(grad_out, coupling, radial, L, rowptr,  \
+                                                         perm, n_nodes, n_edges, channels,       \
+                                                         grad_coupling, grad_radial)
+#define ZS_BWD_STAGED(NQ, FULL)                                                                  \
+    zs_bwd_staged_kernel<NQ, FULL><<<gx, 64, 0, stream>>>(grad_out, coupling, radial, L, rowptr,   \
                                                          perm, n_nodes, n_edges, channels,       \
                                                          grad_coupling, grad_radial)
     if (vec4) {
-#define ZS_BWD_STAGED(NQ, FULL)                                                                  \
-    zs_bwd_staged_kernel<NQ, FULL><<<gx, 64, 0, stream>>>(grad_out, coupling, radial, rowptr, perm, \
-                                                         n_nodes, n_edges, channels,             \
-                                                         grad_coupling, grad_radial)
         if (channels == 32)
             ZS_BWD_STAGED(8, true);
         else if (channels < 32)
@@ -472,7 +471,6 @@ hipError_t launch_backward(const float* grad_out, const float* coupling, const f
             ZS_BWD_STAGED(16, true);
         else if (channels < 64)
             ZS_BWD_STAGED(16, false);
-#undef ZS_BWD_STAGED
         else
             ZS_BWD_LAUNCH(4, 16, false);
     } else {
@@ -481,6 +479,7 @@ hipError_t launch_backward(const float* grad_out, const float* coupling, const f
         else
             ZS_BWD_LAUNCH(1, 16, false);
     }
+#undef ZS_BWD_STAGED
 #undef ZS_BWD_LAUNCH
     return hipGetLastError();
 }

@@ -28,7 +28,7 @@ namespace {
 
 template <int VEC, int NQ, int U>
 __global__ __launch_bounds__(64) void zs_fwd_kernel(const float* __restrict__ coupling,
-                                                    const float* __restrict__ radial,
+                                                    const float* __restrict__ radial, InLayout L,
                                                     const int32_t* __restrict__ rowptr,
                                                     const int32_t* __restrict__ perm,
                                                     int64_t n_nodes, int64_t n_edges, int64_t C,
@@ -49,7 +49,6 @@ __global__ __launch_bounds__(64) void zs_fwd_kernel(const float* __restrict__ co
     const bool two_slots = sA != sB;
     const int64_t c0 = (int64_t(blockIdx.y) * NQ + q) * VEC;
     const bool act = c0 < C;
-    const int64_t row_stride = int64_t(kSlots) * C;
 
     for (int64_t node = blockIdx.x; node < n_nodes; node += gridDim.x) {
         int64_t k0 = rowptr[node];
@@ -75,10 +74,10 @@ __global__ __launch_bounds__(64) void zs_fwd_kernel(const float* __restrict__ co
 #pragma unroll
             for (int b = 0; b < U; ++b) {
                 if (e[b] >= 0 && act) {
-                    const float* rrow = radial + int64_t(e[b]) * row_stride + c0;
-                    xa[b] = V::load(rrow + sA * C);
-                    xb[b] = two_slots ? V::load(rrow + sB * C) : xa[b];
-                    const float* crow = coupling + int64_t(e[b]) * kZonal;
+                    const float* rrow = radial + int64_t(e[b]) * L.rad_edge + c0;
+                    xa[b] = V::load(rrow + sA * L.rad_slot);
+                    xb[b] = two_slots ? V::load(rrow + sB * L.rad_slot) : xa[b];
+                    const float* crow = coupling + int64_t(e[b]) * L.cpl_edge;
 #pragma unroll
                     for (int i = 0; i < RPS; ++i) {
                         const int r = r_first + i;
@@ -191,7 +190,7 @@ __device__ __attribute__((always_inline)) inline int perm_resolve(PermRaw p, int
 __device__ __attribute__((always_inline)) inline void fwd_fetch(FwdRegs& R, int lane, int pe,
                                                                  const float* __restrict__ coupling,
                                                                  const float* __restrict__ radial,
-                                                                 int64_t row_stride, int64_t C,
+                                                                 const InLayout& L, int64_t C,
                                                                  int64_t cbase) {
 #pragma unroll
     for (int i = 0; i < kFwdRadVec; ++i) {
@@ -200,7 +199,8 @@ __device__ __attribute__((always_inline)) inline void fwd_fetch(FwdRegs& R, int 
         const int e = __shfl(pe, fwd_rad_edge(i, lane), 64);
         const int64_t es = e >= 0 ? e : 0;
         const int64_t cs = ch < C ? ch : cbase;
-        R.r[i] = load_stream4<ZS_FWD_NT != 0>(radial + es * row_stride + (rem >> 3) * C + cs);
+        R.r[i] = load_stream4<ZS_FWD_NT != 0>(radial + es * L.rad_edge + (rem >> 3) * L.rad_slot +
+                                              cs);
     }
 #pragma unroll
     for (int i = 0; i < kFwdCplVec; ++i) {
@@ -208,7 +208,7 @@ __device__ __attribute__((always_inline)) inline void fwd_fetch(FwdRegs& R, int 
         const bool in = idx < kFwdBatch * kZonal;
         const int e = __shfl(pe, in ? idx / kZonal : 0, 64);
         const int64_t es = e >= 0 ? e : 0;
-        R.w[i] = coupling[es * kZonal + (in ? idx % kZonal : 0)];
+        R.w[i] = coupling[es * L.cpl_edge + (in ? idx % kZonal : 0)];
     }
 }
 
@@ -248,6 +248,7 @@ __device__ __attribute__((always_inline)) inline void fwd_stage_accumulate(
 
 __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restrict__ coupling,
                                                            const float* __restrict__ radial,
+                                                           InLayout L,
                                                            const int32_t* __restrict__ rowptr,
                                                            const int32_t* __restrict__ perm,
                                                            int64_t n_nodes, int64_t n_edges,
@@ -264,7 +265,6 @@ __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restri
     const int64_t cbase = int64_t(blockIdx.y) * 32;
     const int64_t c0 = cbase + q * 4;
     const bool act = c0 < C;
-    const int64_t row_stride = int64_t(kSlots) * C;
 
     if (lane < kFwdBatch) csh[lane * 16 + 15] = 0.0f;   // pad column, never fetched
 
@@ -286,15 +286,15 @@ __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restri
             FwdRegs RA, RB;
             PermRaw rA = perm_issue(perm, k0, k1, lane, kFwdBatch);
             PermRaw rB = perm_issue(perm, k0 + kFwdBatch, k1, lane, kFwdBatch);
-            fwd_fetch(RA, lane, perm_resolve(rA, n_edges), coupling, radial, row_stride, C, cbase);
+            fwd_fetch(RA, lane, perm_resolve(rA, n_edges), coupling, radial, L, C, cbase);
             for (int64_t t = 0; t < nb; t += 2) {
                 const PermRaw rN = perm_issue(perm, k0 + (t + 2) * kFwdBatch, k1, lane, kFwdBatch);
-                fwd_fetch(RB, lane, perm_resolve(rB, n_edges), coupling, radial, row_stride, C,
+                fwd_fetch(RB, lane, perm_resolve(rB, n_edges), coupling, radial, L, C,
                           cbase);
                 fwd_stage_accumulate(RA, rsh, csh, batch_count(t), lane, q, j, sA, sB, acc0, acc1);
                 if (t + 1 >= nb) break;
                 rB = perm_issue(perm, k0 + (t + 3) * kFwdBatch, k1, lane, kFwdBatch);
-                fwd_fetch(RA, lane, perm_resolve(rN, n_edges), coupling, radial, row_stride, C,
+                fwd_fetch(RA, lane, perm_resolve(rN, n_edges), coupling, radial, L, C,
                           cbase);
                 fwd_stage_accumulate(RB, rsh, csh, batch_count(t + 1), lane, q, j, sA, sB, acc0,
                                      acc1);
@@ -316,20 +316,21 @@ __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restri
 
 }  // namespace
 
-hipError_t launch_forward(const float* coupling, const float* radial, const int32_t* rowptr,
-                          const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels,
-                          float* out, bool vec4, hipStream_t stream) {
+hipError_t launch_forward(const float* coupling, const float* radial, InLayout L,
+                          const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
+                          int64_t n_edges, int64_t channels, float* out, bool vec4,
+                          hipStream_t stream) {
     constexpr int64_t kGridCap = 1 << 20;
     const unsigned gx = unsigned(n_nodes < kGridCap ? n_nodes : kGridCap);
     if (vec4) {
         const unsigned gy = unsigned((channels + 31) / 32);
-        zs_fwd_staged_kernel<<<dim3(gx, gy), 64, 0, stream>>>(coupling, radial, rowptr, perm,
+        zs_fwd_staged_kernel<<<dim3(gx, gy), 64, 0, stream>>>(coupling, radial, L, rowptr, perm,
                                                               n_nodes, n_edges, channels, out);
     } else {
         constexpr int NQ = 16, VEC = 1;
         const unsigned gy = unsigned((channels + NQ * VEC - 1) / (NQ * VEC));
-        zs_fwd_kernel<VEC, NQ, 8><<<dim3(gx, gy), 64, 0, stream>>>(coupling, radial, rowptr, perm,
-                                                                   n_nodes, n_edges, channels, out);
+        zs_fwd_kernel<VEC, NQ, 8><<<dim3(gx, gy), 64, 0, stream>>>(
+            coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out);
     }
     return hipGetLastError();
 }

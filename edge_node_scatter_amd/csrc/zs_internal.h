@@ -90,14 +90,23 @@ hipError_t launch_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int3
                       int32_t* flag, hipStream_t stream);
 
 // ---- forward / backward -----------------------------------------------------
-hipError_t launch_forward(const float* coupling, const float* radial, const int32_t* rowptr,
-                          const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels,
-                          float* out, bool vec4, hipStream_t stream);
+// Strides (in floats) of the two edge inputs.  Coupling columns and radial
+// channels are unit-stride; a contiguous layout is {15, 3*C, C}.
+struct InLayout {
+    int64_t cpl_edge;   // coupling: edge -> edge
+    int64_t rad_edge;   // radial: edge -> edge
+    int64_t rad_slot;   // radial: slot -> slot
+};
+
+hipError_t launch_forward(const float* coupling, const float* radial, InLayout L,
+                          const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
+                          int64_t n_edges, int64_t channels, float* out, bool vec4,
+                          hipStream_t stream);
 
 hipError_t launch_backward(const float* grad_out, const float* coupling, const float* radial,
-                           const int32_t* dst32, const int32_t* rowptr, const int32_t* perm,
-                           int64_t n_nodes, int64_t n_edges, int64_t channels,
-                           float* grad_coupling, float* grad_radial, bool vec4,
+                           InLayout L, const int32_t* dst32, const int32_t* rowptr,
+                           const int32_t* perm, int64_t n_nodes, int64_t n_edges,
+                           int64_t channels, float* grad_coupling, float* grad_radial, bool vec4,
                            hipStream_t stream);
 
 // Small fill kernel (used instead of hipMemsetAsync so the calls stay

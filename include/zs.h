@@ -142,6 +142,42 @@ int zs_backward(const float *grad_out, const float *coupling,
                 int64_t n_edges, int64_t channels, float *grad_coupling,
                 float *grad_radial, void *stream);
 
+/*
+ * zs_forward_strided / zs_backward_strided -- the same operations on strided
+ * views of the two edge inputs, so callers need not copy them to contiguous
+ * buffers first.  The GIE page's test suite feeds the operator sliced views of
+ * the radial features (section "Tests"), and the band page (deepmd-kit PR
+ * #6071, "banded Wigner-D storage for the fused inference consumers",
+ * Summary) stores each edge's rotation as a packed (E, 3D-2) band whose
+ * m = 0 segment is the zonal coupling, i.e. a coupling view with an edge
+ * stride of 46 floats.
+ *
+ *   coupling[e][j]   is read at coupling[e * coupling_edge_stride + j]
+ *   radial[e][s][c]  is read at radial[e * radial_edge_stride +
+ *                                      s * radial_slot_stride + c]
+ *
+ * Strides are in floats and must be >= 0 (else ZS_ERR_SHAPE); inputs are
+ * only read, so overlapping or broadcast (stride 0) rows are allowed.  Outputs
+ * are contiguous as in zs_forward/zs_backward, must not overlap the strided
+ * inputs' extents, and results are identical to those calls on contiguous
+ * copies of the views.
+ * Radial strides that are multiples of 4 (with a 16-byte aligned base) keep
+ * the vector kernels.
+ */
+int zs_forward_strided(const float *coupling, int64_t coupling_edge_stride,
+                       const float *radial, int64_t radial_edge_stride,
+                       int64_t radial_slot_stride, const int32_t *rowptr,
+                       const int32_t *perm, int64_t n_nodes, int64_t n_edges,
+                       int64_t channels, float *out, void *stream);
+
+int zs_backward_strided(const float *grad_out, const float *coupling,
+                        int64_t coupling_edge_stride, const float *radial,
+                        int64_t radial_edge_stride, int64_t radial_slot_stride,
+                        const int32_t *dst32, const int32_t *rowptr,
+                        const int32_t *perm, int64_t n_nodes, int64_t n_edges,
+                        int64_t channels, float *grad_coupling,
+                        float *grad_radial, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,8 @@ def lib():
 def test_header_symbols_exported(lib):
     declared = zs.declared_symbols()
     assert set(declared) == {"zs_status_string", "zs_csr_workspace_bytes", "zs_build_csr",
-                             "zs_forward", "zs_backward"}
+                             "zs_forward", "zs_backward", "zs_forward_strided",
+                             "zs_backward_strided"}
     out = subprocess.check_output(["nm", "-D", "--defined-only", zs.LIB_PATH], text=True)
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for name in declared:
@@ -93,6 +94,31 @@ def test_backward_rejects(lib):
     assert f(A, B, C_, D, D + 4096, D + 8192, 4, 10, 32, W, C_ + 256, None) == ZS_ERR_ALIAS
     # no edges: nothing to write, returns before touching the device
     assert f(A, B, C_, D, D + 4096, D + 8192, 4, 0, 32, W, X, None) == 0
+
+
+def test_strided_rejects(lib):
+    f, b = lib.zs_forward_strided, lib.zs_backward_strided
+    assert f(A, -1, B, 96, 32, C_, D, 4, 10, 32, X, None) == ZS_ERR_SHAPE      # negative stride
+    assert f(A, 15, B, -96, 32, C_, D, 4, 10, 32, X, None) == ZS_ERR_SHAPE
+    assert f(A, 15, B, 96, -32, C_, D, 4, 10, 32, X, None) == ZS_ERR_SHAPE
+    assert f(A, 46, B, 160, 32, C_, D, 4, 10, 0, X, None) == ZS_ERR_SHAPE      # channels
+    assert f(None, 46, B, 160, 32, C_, D, 4, 10, 32, X, None) == ZS_ERR_NULL
+    # out inside the strided radial extent (9*160 + 2*32 + 32 floats) -> alias
+    assert f(A, 46, B, 160, 32, C_, D, 4, 10, 32, B + 4 * 1500, None) == ZS_ERR_ALIAS
+    # out inside the strided coupling extent (9*46 + 15 floats) -> alias
+    assert f(A, 46, B, 160, 32, C_, D, 4, 10, 32, A + 4 * 420, None) == ZS_ERR_ALIAS
+    assert b(A, B, -46, C_, 160, 32, D, D + 4096, D + 8192, 4, 10, 32, W, X, None) == ZS_ERR_SHAPE
+    assert b(A, B, 46, C_, 160, 32, D, D + 4096, D + 8192, 4, 10, 32, W, C_ + 4 * 1500,
+             None) == ZS_ERR_ALIAS
+    assert b(A, B, 46, C_, 160, 32, D, D + 4096, D + 8192, 4, 0, 32, W, X, None) == 0
+
+
+def test_band_view_helper():
+    import torch
+    band = torch.arange(5 * 46, dtype=torch.float32).reshape(5, 46)
+    c = zs.coupling_from_band(band)
+    assert c.shape == (5, 15) and c.stride() == (46, 1)
+    assert torch.equal(c[:, 0], band[:, 16]) and torch.equal(c[:, 14], band[:, 30])
 
 
 def test_binding_refuses_cpu_tensors():

@@ -279,3 +279,53 @@ def test_autograd_function_sliced_radial(dev):
         assert np.array_equal(_bits(out.detach().cpu().numpy()), _bits(ref_out))
         assert np.array_equal(_bits(rad.grad.cpu().numpy()), _bits(ref_gr))
         check_grad_coupling(cpl.grad.cpu().numpy(), ref_gc, "autograd grad_coupling")
+
+
+STRIDED_CASES = [
+    # (label, N, E, C, radial slab width (slots in the wider tensor), radial slot offset, band)
+    ("sliced_radial_c32", 64, 3000, 32, 5, 1, False),
+    ("band_coupling_c32", 64, 3000, 32, 3, 0, True),
+    ("both_c32", 300, 20000, 32, 4, 1, True),
+    ("both_c64", 50, 5000, 64, 6, 2, True),
+    ("sliced_c40", 33, 777, 40, 5, 1, True),
+    ("odd_stride_c33", 20, 900, 33, 4, 1, True),          # strides not multiples of 4
+    ("sliced_c36", 20, 900, 36, 4, 1, False),
+]
+
+
+def _strided_inputs(x, dev, slab, s0, band):
+    """Views of wider device tensors that hold the workload's inputs."""
+    E, C = x["radial"].shape[0], x["radial"].shape[2]
+    rng = np.random.default_rng(E + C)
+    wide = torch.from_numpy(rng.standard_normal((E, slab, C + (1 if C % 2 else 0)),
+                                                dtype=np.float32)).to(dev)
+    wide[:, s0:s0 + 3, :C] = torch.from_numpy(x["radial"]).to(dev)
+    rad = wide[:, s0:s0 + 3, :C]
+    if band:
+        b = torch.from_numpy(rng.standard_normal((E, 46), dtype=np.float32)).to(dev)
+        cpl = zs.coupling_from_band(b)
+        cpl.copy_(torch.from_numpy(x["coupling"]).to(dev))
+    else:
+        cpl = torch.from_numpy(x["coupling"]).to(dev)
+    return cpl, rad
+
+
+@pytest.mark.parametrize("label,N,E,C,slab,s0,band", STRIDED_CASES,
+                         ids=[c[0] for c in STRIDED_CASES])
+def test_strided_views(dev, label, N, E, C, slab, s0, band):
+    """Sliced radial features and the coupling inside a packed (E, 46) band are
+    read in place and give the oracle's results for the contiguous inputs."""
+    w = synthetic.custom(label, N, E, C, seed=5000 + E + C, envelope=True)
+    x = synthetic.make_inputs(w)
+    say(f"[gpu] strided views {label}: N={N} E={E} C={C}")
+    cpl, rad = _strided_inputs(x, dev, slab, s0, band)
+    assert not rad.is_contiguous() or not cpl.is_contiguous()
+    csr = zs.zs_build_csr(torch.from_numpy(x["dst"]).to(dev), N)
+    out = zs.zs_forward(cpl, rad, csr)
+    gc, gr = zs.zs_backward(torch.from_numpy(x["grad_out"]).to(dev), cpl, rad, csr)
+    torch.cuda.synchronize()
+    ref_out = oracle.forward(x["coupling"], x["radial"], x["dst"], N)
+    ref_gc, ref_gr = oracle.backward(x["grad_out"], x["coupling"], x["radial"], x["dst"])
+    assert np.array_equal(_bits(out.cpu().numpy()), _bits(ref_out)), f"{label}: forward"
+    assert np.array_equal(_bits(gr.cpu().numpy()), _bits(ref_gr)), f"{label}: grad_radial"
+    check_grad_coupling(gc.cpu().numpy(), ref_gc, f"{label}: grad_coupling")
