@@ -177,6 +177,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline", choices=sorted(synthetic.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--inputs", default="contiguous", choices=["contiguous", "views"],
+                    help="views: coupling read in place from a packed (E, 46) Wigner band and "
+                         "radial features sliced from an (E, 5, C) tensor (strided entry points)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize two rocprofv3 --pmc counter_collection.csv files "
                          "(FETCH_SIZE, WRITE_SIZE) into profiles/traffic_headline.json and exit")
@@ -201,10 +204,18 @@ def main() -> int:
     dev = torch.device("cuda:0")
     zs.load()
     dst = torch.from_numpy(x["dst"]).to(dev)
-    cpl = torch.from_numpy(x["coupling"]).to(dev)
-    rad = torch.from_numpy(x["radial"]).to(dev)
-    g = torch.from_numpy(x["grad_out"]).to(dev)
     E, N, C = w.n_edges, w.n_nodes, w.channels
+    if args.inputs == "views":
+        band = torch.zeros((E, 3 * 16 - 2), device=dev)
+        cpl = zs.coupling_from_band(band)
+        cpl.copy_(torch.from_numpy(x["coupling"]).to(dev))
+        wide = torch.zeros((E, 5, C), device=dev)
+        rad = wide[:, 1:4]
+        rad.copy_(torch.from_numpy(x["radial"]).to(dev))
+    else:
+        cpl = torch.from_numpy(x["coupling"]).to(dev)
+        rad = torch.from_numpy(x["radial"]).to(dev)
+    g = torch.from_numpy(x["grad_out"]).to(dev)
     csr = zs.Csr(torch.empty(N + 1, dtype=torch.int32, device=dev),
                  torch.empty(E, dtype=torch.int32, device=dev),
                  torch.empty(E, dtype=torch.int32, device=dev), N)
@@ -270,6 +281,7 @@ def main() -> int:
         "config": {
             "workload": f"{w.name}: N={N} nodes, E={E} edges, C={C} channels, lmax=3, fp32",
             "n_nodes": N, "n_edges": E, "channels": C, "dst": w.dst_kind,
+            "inputs": args.inputs,
         },
         "fwd_bwd_us": round(fb_us, 2),
         "fwd_us": round(fwd_us, 2),

@@ -1,0 +1,69 @@
+"""Instruction-level checks on the gfx950 code of this library (CPU only).
+
+The forward and grad_radial must add separately rounded fp32 products (no
+fused multiply-add), so the fp32 kernels may contain no v_fma_f32 /
+v_fmac_f32 / v_fma_mix and no packed fp32 VALU instructions; the hot kernels
+must not spill to scratch.  The assembly is produced from the sources with the
+library's own flags (hipcc --cuda-device-only -S).
+"""
+import os
+import re
+
+import pytest
+
+from edge_node_scatter_amd import build as zs_build
+
+HOT = ("zs_fwd_staged_kernel", "zs_bwd_staged_kernel", "zs_fwd_kernel", "zs_bwd_kernel")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("asm")
+    texts = {}
+    for path in zs_build.device_asm(str(out)):
+        texts[os.path.basename(path)] = open(path).read()
+    return texts
+
+
+def _kernels(text):
+    """{symbol: body} for every kernel in an assembly file."""
+    bodies = {}
+    for m in re.finditer(r"^(_Z\S+):[^\n]*\n(.*?)^\s*s_endpgm", text, flags=re.M | re.S):
+        bodies[m.group(1)] = m.group(2)
+    return bodies
+
+
+def _meta(text, sym):
+    m = re.search(r"\.name:\s+" + re.escape(sym) + r"\s*\n(.*?)(?=\n\s+- \.|\n\s*\.\.\.|\Z)",
+                  text, flags=re.S)
+    return m.group(1) if m else ""
+
+
+def test_no_fp32_fma_or_packed_ops(asm):
+    seen = 0
+    for name in ("zs_fwd-gfx950.s", "zs_bwd-gfx950.s"):
+        for sym, body in _kernels(asm[name]).items():
+            seen += 1
+            bad = re.findall(r"\b(v_fmac?_f32|v_fma_mix\w*|v_pk_(?:fma|mul|add)_f32|v_mad_f32)\b",
+                             body)
+            assert not bad, f"{sym}: {sorted(set(bad))}"
+    assert seen >= 4
+
+
+def test_fp64_channel_sums_use_fma(asm):
+    body = "".join(b for s, b in _kernels(asm["zs_bwd-gfx950.s"]).items()
+                   if "zs_bwd_staged_kernel" in s)
+    assert "v_fma_f64" in body or "v_fmac_f64" in body
+
+
+def test_hot_kernels_do_not_spill(asm):
+    for name in ("zs_fwd-gfx950.s", "zs_bwd-gfx950.s"):
+        text = asm[name]
+        for sym in _kernels(text):
+            if not any(h in sym for h in HOT):
+                continue
+            meta = _meta(text, sym)
+            spill = re.search(r"\.vgpr_spill_count:\s+(\d+)", meta)
+            priv = re.search(r"\.private_segment_fixed_size:\s+(\d+)", meta)
+            assert spill and int(spill.group(1)) == 0, f"{sym} spills VGPRs"
+            assert priv and int(priv.group(1)) == 0, f"{sym} uses scratch"
