@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "zs_oracle.c")
 _LIB = os.path.join(_HERE, "libzs_oracle.so")
 
-GCC_FLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+GCC_FLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-fno-builtin-sqrt",
              "-fno-fast-math", "-fexcess-precision=standard", "-Wall", "-Werror"]
 
 
@@ -28,7 +28,7 @@ def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
     """Compile the oracle library with gcc (no GPU involved)."""
     if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
         tmp = out + ".tmp"
-        subprocess.check_call(["gcc", *GCC_FLAGS, src, "-o", tmp])
+        subprocess.check_call(["gcc", *GCC_FLAGS, src, "-o", tmp, "-lm"])
         os.replace(tmp, out)
     return out
 
@@ -41,6 +41,9 @@ _SIGS = {
     "zs_oracle_forward_f64": "PPPIIIP",
     "zs_oracle_backward_f64": "PPPPIIIPP",
     "zs_oracle_csr": "PIIPPP",
+    "zs_oracle_forward_norm_f32": "PPPPIIIPPP",
+    "zs_oracle_backward_norm_f32": "PPPPPPIIIPPPP",
+    "zs_oracle_forward_norm_f64": "PPPPIIIPP",
 }
 
 
@@ -123,6 +126,41 @@ class Oracle:
                                                      len(edges), _p(gc), _p(gr)))
         return gc, gr
 
+    def forward_norm(self, coupling, radial, env, dst, n_nodes, dtype=np.float32):
+        """Scatter followed by the 1/sqrt(degree) normalisation.
+
+        fp32: (y, out, norm); fp64: (y, norm)."""
+        dst, coupling, radial, E, C = _prep(dst, coupling, radial)
+        env = np.ascontiguousarray(env, dtype=np.float32)
+        if env.shape != (E,):
+            raise ValueError("env must be (E,)")
+        y = np.empty((n_nodes, 16, C), dtype=dtype)
+        norm = np.empty(n_nodes, dtype=dtype)
+        if dtype == np.float64:
+            _check(self.lib.zs_oracle_forward_norm_f64(_p(coupling), _p(radial), _p(env), _p(dst),
+                                                       E, n_nodes, C, _p(y), _p(norm)))
+            return y, norm
+        out = np.empty((n_nodes, 16, C), dtype=np.float32)
+        _check(self.lib.zs_oracle_forward_norm_f32(_p(coupling), _p(radial), _p(env), _p(dst), E,
+                                                   n_nodes, C, _p(y), _p(out), _p(norm)))
+        return y, out, norm
+
+    def backward_norm(self, grad_y, out, norm, coupling, radial, dst):
+        """(grad_coupling, grad_radial, grad_env) of the normalised scatter (fp32)."""
+        dst, coupling, radial, E, C = _prep(dst, coupling, radial)
+        grad_y = np.ascontiguousarray(grad_y, dtype=np.float32)
+        out = np.ascontiguousarray(out, dtype=np.float32)
+        norm = np.ascontiguousarray(norm, dtype=np.float32)
+        N = grad_y.shape[0]
+        gc = np.empty((E, 15), dtype=np.float32)
+        gr = np.empty((E, 3, C), dtype=np.float32)
+        ge = np.empty(E, dtype=np.float32)
+        scratch = np.empty((N, 16, C), dtype=np.float32)
+        _check(self.lib.zs_oracle_backward_norm_f32(_p(grad_y), _p(out), _p(norm), _p(coupling),
+                                                    _p(radial), _p(dst), E, N, C, _p(gc), _p(gr),
+                                                    _p(ge), _p(scratch)))
+        return gc, gr, ge
+
     def csr(self, dst, n_nodes):
         """(rowptr (N+1,) int32, perm (E,) int32): stable counting sort by dst."""
         dst = np.ascontiguousarray(dst, dtype=np.int64)
@@ -164,3 +202,11 @@ def backward_edges(*a, **k):
 
 def csr(*a, **k):
     return get().csr(*a, **k)
+
+
+def forward_norm(*a, **k):
+    return get().forward_norm(*a, **k)
+
+
+def backward_norm(*a, **k):
+    return get().backward_norm(*a, **k)

@@ -47,6 +47,7 @@
  *
  * Return values: 0 on success, -3 when a destination index is out of range.
  */
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -276,5 +277,103 @@ int zs_oracle_csr(const int64_t *dst, int64_t E, int64_t N, int32_t *rowptr,
         cursor[n] = rowptr[n];
     for (int64_t e = 0; e < E; ++e)          /* increasing e keeps ties stable */
         perm[cursor[dst[e]]++] = (int32_t)e;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Degree normalisation applied after the scatter.                           */
+/*                                                                           */
+/* The GIE page keeps an inverse-square-root degree normalisation right      */
+/* after the scatter, with its own cotangent because the degree depends on   */
+/* the cutoff envelope, i.e. on geometry ("What", third bullet; last step of */
+/* the sequence diagram).  Reading used here:                                */
+/*   deg[n]  = sum of env[e] over the edges of n (fp32, edge order, from +0) */
+/*   norm[n] = 1 / sqrt(deg[n])  (fp32 sqrt, then fp32 division),            */
+/*             0 when deg[n] <= 0                                            */
+/*   y[n][r][c] = out[n][r][c] * norm[n]  (fp32)                             */
+/* Backward, gy being the upstream gradient of y:                            */
+/*   g_out[n][r][c] = gy[n][r][c] * norm[n]  (fp32), then the scatter        */
+/*                    backward above with g_out as upstream gradient         */
+/*   ddeg[n] = -1/2 * t*t*t * s, t = norm[n] (fp64, left to right), where    */
+/*             s = sum over r = 1..15, c of gy[n][r][c] * out[n][r][c]       */
+/*             (exact products, fp64 sum over r then c); rounded to fp32     */
+/*             once; 0 when norm[n] == 0                                     */
+/*   grad_env[e] = ddeg[dst[e]]                                              */
+/* ------------------------------------------------------------------------- */
+int zs_oracle_forward_norm_f32(const float *coupling, const float *radial,
+                               const float *env, const int64_t *dst, int64_t E,
+                               int64_t N, int64_t C, float *y, float *out,
+                               float *norm)
+{
+    const int rc = zs_oracle_forward_f32(coupling, radial, dst, E, N, C, out);
+    if (rc)
+        return rc;
+    for (int64_t n = 0; n < N; ++n)
+        norm[n] = 0.0f;                      /* used as the degree accumulator */
+    for (int64_t e = 0; e < E; ++e)
+        norm[dst[e]] = norm[dst[e]] + env[e];
+    for (int64_t n = 0; n < N; ++n) {
+        const float deg = norm[n];
+        if (deg > 0.0f) {
+            const float root = sqrtf(deg);
+            norm[n] = 1.0f / root;
+        } else {
+            norm[n] = 0.0f;
+        }
+    }
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t i = 0; i < ZS_ORACLE_ROWS * C; ++i)
+            y[n * ZS_ORACLE_ROWS * C + i] = out[n * ZS_ORACLE_ROWS * C + i] * norm[n];
+    return 0;
+}
+
+int zs_oracle_backward_norm_f32(const float *grad_y, const float *out,
+                                const float *norm, const float *coupling,
+                                const float *radial, const int64_t *dst,
+                                int64_t E, int64_t N, int64_t C,
+                                float *grad_coupling, float *grad_radial,
+                                float *grad_env, float *grad_out_scratch)
+{
+    if (check_dst(dst, E, N))
+        return -3;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t i = 0; i < ZS_ORACLE_ROWS * C; ++i)
+            grad_out_scratch[n * ZS_ORACLE_ROWS * C + i] =
+                grad_y[n * ZS_ORACLE_ROWS * C + i] * norm[n];
+    const int rc = zs_oracle_backward_f32(grad_out_scratch, coupling, radial, dst,
+                                          E, N, C, grad_coupling, grad_radial);
+    if (rc)
+        return rc;
+    for (int64_t e = 0; e < E; ++e) {
+        const int64_t n = dst[e];
+        double s = 0.0;
+        for (int r = 1; r < ZS_ORACLE_ROWS; ++r)
+            for (int64_t c = 0; c < C; ++c) {
+                const int64_t i = (n * ZS_ORACLE_ROWS + r) * C + c;
+                s = s + (double)grad_y[i] * (double)out[i];
+            }
+        const double t = norm[n];
+        grad_env[e] = t == 0.0 ? 0.0f : (float)(-0.5 * t * t * t * s);
+    }
+    return 0;
+}
+
+/* fp64 versions for the pins: the same reading with every step in double. */
+int zs_oracle_forward_norm_f64(const float *coupling, const float *radial,
+                               const float *env, const int64_t *dst, int64_t E,
+                               int64_t N, int64_t C, double *y, double *norm)
+{
+    const int rc = zs_oracle_forward_f64(coupling, radial, dst, E, N, C, y);
+    if (rc)
+        return rc;
+    for (int64_t n = 0; n < N; ++n)
+        norm[n] = 0.0;
+    for (int64_t e = 0; e < E; ++e)
+        norm[dst[e]] = norm[dst[e]] + (double)env[e];
+    for (int64_t n = 0; n < N; ++n)
+        norm[n] = norm[n] > 0.0 ? 1.0 / sqrt(norm[n]) : 0.0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t i = 0; i < ZS_ORACLE_ROWS * C; ++i)
+            y[n * ZS_ORACLE_ROWS * C + i] = y[n * ZS_ORACLE_ROWS * C + i] * norm[n];
     return 0;
 }

@@ -118,7 +118,8 @@ def make_inputs(w: Workload | str, with_grad: bool = True) -> dict:
     """All operator inputs for workload ``w`` as contiguous numpy arrays.
 
     dst      (E,)          int64
-    coupling (E, 15)       float32, U(-1,1) (times U(0,1) envelope when enabled)
+    env      (E,)          float32, U(0,1) per-edge cutoff envelope factor
+    coupling (E, 15)       float32, U(-1,1) (times env when the workload has one)
     radial   (E, 3, C)     float32, N(0,1)
     grad_out (N, 16, C)    float32, N(0,1)   (upstream gradient of the output)
     """
@@ -126,10 +127,12 @@ def make_inputs(w: Workload | str, with_grad: bool = True) -> dict:
         w = WORKLOADS[w]
     E, N, C = w.n_edges, w.n_nodes, w.channels
     out = {"workload": w, "dst": make_dst(w)}
+    env = _rng(w.seed, _TAG_ENV).uniform(0.0, 1.0, size=E)
     cpl = _rng(w.seed, _TAG_COUPLING).uniform(-1.0, 1.0, size=(E, ZONAL))
     if w.envelope:
-        cpl = cpl * _rng(w.seed, _TAG_ENV).uniform(0.0, 1.0, size=(E, 1))
+        cpl = cpl * env[:, None]
     out["coupling"] = np.ascontiguousarray(cpl.astype(np.float32))
+    out["env"] = env.astype(np.float32)
     out["radial"] = _rng(w.seed, _TAG_RADIAL).standard_normal(size=(E, SLOTS, C), dtype=np.float32)
     if with_grad:
         out["grad_out"] = _rng(w.seed, _TAG_GRAD).standard_normal(size=(N, ROWS, C), dtype=np.float32)

@@ -16,7 +16,11 @@ oracle disagrees with something the pages or the mathematics fix:
 * the backward: adjoint identity, an explicit Jacobian on a tiny problem,
   finite differences, exact rational sums for the channel reduction, the
   fp32 grad_radial order, and insensitivity to upstream row 0;
-* the CSR: a library stable argsort and a brute-force scan.
+* the CSR: a library stable argsort and a brute-force scan;
+* the degree normalisation: unit envelopes (neighbour counts, closed-form
+  1/sqrt), exact halving when every envelope is multiplied by 4, the fp64
+  evaluation, finite differences of all three gradients, and insensitivity
+  to upstream rows that cannot matter.
 
 Sizes are small so the whole set runs in a few seconds; ``test_oracle_pins``
 runs it on the committed oracle and ``test_oracle_mutants`` runs it on copies
@@ -381,6 +385,107 @@ def _golden(name):
                 k, v = line.split("=", 1)
                 fx[k.strip()] = v.strip()
     return fx
+
+
+
+
+# --------------------------------------------------------------------------- degree normalisation
+def _norm_problem(seed, E, N, C):
+    dst, cpl, rad, g = _problem(seed, E, N, C)
+    env = _rng(seed + 1).uniform(0.05, 1.0, size=E).astype(np.float32)
+    return dst, cpl, rad, g, env
+
+
+def pin_norm_unit_envelope(orc):
+    """Unit envelopes: deg = neighbour count, norm = 1/sqrt(count) (one fp32
+    sqrt and one fp32 division), empty nodes get 0; y against fp64 brute force."""
+    E, N, C = 400, 23, 6
+    dst = _rng(91).integers(0, N - 3, size=E).astype(np.int64)        # 3 empty nodes
+    _, cpl, rad, _ = _problem(92, E, N, C, dst=dst)
+    y, out, norm = orc.forward_norm(cpl, rad, np.ones(E, np.float32), dst, N)
+    cnt = np.bincount(dst, minlength=N).astype(np.float32)
+    want = np.zeros(N, np.float32)
+    nz = cnt > 0
+    want[nz] = np.float32(1.0) / np.sqrt(cnt[nz])
+    _assert_bitwise(norm, want, "norm with unit envelopes")
+    ref = (_incidence(dst, N) @ _message64(cpl, rad).reshape(E, -1)).reshape(N, 15, C)
+    ref = ref / np.where(cnt > 0, np.sqrt(cnt.astype(np.float64)), np.inf)[:, None, None]
+    mag = (_incidence(dst, N) @ np.abs(_message64(cpl, rad)).reshape(E, -1)).reshape(N, 15, C)
+    bound = (cnt[:, None, None] + 6) * U32 * mag / np.maximum(np.sqrt(cnt), 1)[:, None, None]
+    assert np.all(np.abs(y[:, 1:].astype(np.float64) - ref) <= bound + 1e-30), "y vs brute force"
+    assert np.all(_bits(y[:, 0]) == 0) and np.all(_bits(y[~nz]) == 0), "row 0 / empty nodes"
+
+
+def pin_norm_envelope_scaling(orc):
+    """Envelopes times 4: every degree times 4, norm halved exactly, y halved."""
+    E, N, C = 300, 11, 5
+    dst, cpl, rad, _, env = _norm_problem(93, E, N, C)
+    y1, _, n1 = orc.forward_norm(cpl, rad, env, dst, N)
+    y4, _, n4 = orc.forward_norm(cpl, rad, env * np.float32(4), dst, N)
+    _assert_bitwise(n4, n1 * np.float32(0.5), "norm(4 env) = norm(env)/2")
+    _assert_bitwise(y4, y1 * np.float32(0.5), "y(4 env) = y(env)/2")
+
+
+def pin_norm_matches_fp64(orc):
+    E, N, C = 500, 17, 7
+    dst, cpl, rad, _, env = _norm_problem(94, E, N, C)
+    y, _, norm = orc.forward_norm(cpl, rad, env, dst, N)
+    y64, norm64 = orc.forward_norm(cpl, rad, env, dst, N, dtype=np.float64)
+    assert np.allclose(norm, norm64, rtol=8 * U32, atol=0), "norm vs fp64"
+    deg = np.bincount(dst, minlength=N)[:, None, None]
+    absm = (_incidence(dst, N) @ np.abs(_message64(cpl, rad)).reshape(E, -1)).reshape(N, 15, C)
+    bound = (deg + 6) * U32 * absm * norm64[:, None, None] + 1e-30
+    assert np.all(np.abs(y[:, 1:] - y64[:, 1:]) <= bound), "y vs fp64"
+
+
+def pin_norm_backward_finite_difference(orc):
+    """Gradients of L = <gy, y> by central differences of the fp64 forward."""
+    E, N, C = 240, 9, 4
+    dst, cpl, rad, gy, env = _norm_problem(95, E, N, C)
+    y, out, norm = orc.forward_norm(cpl, rad, env, dst, N)
+    gc, gr, ge = orc.backward_norm(gy, out, norm, cpl, rad, dst)
+    g64 = gy.astype(np.float64)
+
+    def loss(c, r, v):
+        return float(np.sum(g64 * orc.forward_norm(c, r, v, dst, N, dtype=np.float64)[0]))
+
+    rng = _rng(96)
+    for _ in range(10):
+        e = rng.integers(E)
+        h = np.float32(1.0 / 64)
+        vp, vm = env.copy(), env.copy()
+        vp[e] += h
+        vm[e] -= h
+        fd = (loss(cpl, rad, vp) - loss(cpl, rad, vm)) / (float(vp[e]) - float(vm[e]))
+        assert abs(fd - ge[e]) <= 1e-4 * abs(fd) + 1e-5, f"grad_env[{e}]: {ge[e]} vs FD {fd}"
+        j = rng.integers(15)
+        cp, cm = cpl.copy(), cpl.copy()
+        cp[e, j] += np.float32(0.5)
+        cm[e, j] -= np.float32(0.5)
+        fd = (loss(cp, rad, env) - loss(cm, rad, env)) / (float(cp[e, j]) - float(cm[e, j]))
+        assert abs(fd - gc[e, j]) <= 1e-5 * abs(fd) + 1e-6, "grad_coupling (normalised)"
+        s, c = rng.integers(3), rng.integers(C)
+        rp, rm = rad.copy(), rad.copy()
+        rp[e, s, c] += np.float32(0.5)
+        rm[e, s, c] -= np.float32(0.5)
+        fd = (loss(cpl, rp, env) - loss(cpl, rm, env)) / (float(rp[e, s, c]) - float(rm[e, s, c]))
+        assert abs(fd - gr[e, s, c]) <= 1e-5 * abs(fd) + 1e-6, "grad_radial (normalised)"
+
+
+def pin_norm_backward_zero_degree_rows(orc):
+    """Upstream gradient on nodes without edges and on row 0 changes nothing."""
+    E, N, C = 150, 12, 5
+    dst = _rng(97).integers(0, N - 4, size=E).astype(np.int64)
+    _, cpl, rad, gy = _problem(98, E, N, C, dst=dst)
+    env = _rng(99).uniform(0.1, 1.0, size=E).astype(np.float32)
+    y, out, norm = orc.forward_norm(cpl, rad, env, dst, N)
+    a = orc.backward_norm(gy, out, norm, cpl, rad, dst)
+    g2 = gy.copy()
+    g2[N - 4:] = np.float32(7.0)
+    g2[:, 0] = np.float32(-3.0)
+    b = orc.backward_norm(g2, out, norm, cpl, rad, dst)
+    for u, v, what in zip(a, b, ("grad_coupling", "grad_radial", "grad_env")):
+        _assert_bitwise(u, v, what)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -67,6 +67,15 @@ MUTANTS = [
     ("csr_off_by_one", "rowptr[dst[e] + 1] += 1;", "rowptr[dst[e]] += 1;", 0),
     ("csr_unstable", "for (int64_t e = 0; e < E; ++e)          /* increasing e keeps ties stable */",
      "for (int64_t e = E - 1; e >= 0; --e)", 0),
+    ("norm_grad_factor", "(float)(-0.5 * t * t * t * s)", "(float)(-1.0 * t * t * t * s)", 0),
+    ("norm_grad_power", "(float)(-0.5 * t * t * t * s)", "(float)(-0.5 * t * t * s)", 0),
+    ("norm_grad_unscaled", "grad_y[n * ZS_ORACLE_ROWS * C + i] * norm[n];",
+     "grad_y[n * ZS_ORACLE_ROWS * C + i];", 0),
+    ("norm_not_inverse", "norm[n] = 1.0f / root;", "norm[n] = root;", 0),
+    ("norm_counts_edges", "norm[dst[e]] = norm[dst[e]] + env[e];",
+     "norm[dst[e]] = norm[dst[e]] + 1.0f;", 0),
+    ("norm_y_unscaled", "y[n * ZS_ORACLE_ROWS * C + i] = out[n * ZS_ORACLE_ROWS * C + i] * norm[n];",
+     "y[n * ZS_ORACLE_ROWS * C + i] = out[n * ZS_ORACLE_ROWS * C + i];", 0),
     ("no_index_check", "if (dst[e] < 0 || dst[e] >= N)\n            return -3;",
      "if (dst[e] < 0 && dst[e] >= N)\n            return -3;", 0),
 ]
