@@ -10,6 +10,9 @@ Functions carry the C ABI's names:
 * ``zs_build_csr(dst, n_nodes)`` -> ``Csr(rowptr, perm, dst32)``
 * ``zs_forward(coupling, radial, csr)`` -> out (N, 16, C)
 * ``zs_backward(grad_out, coupling, radial, csr)`` -> (grad_coupling, grad_radial)
+* ``zs_forward_normalized(coupling, radial, env, csr)`` -> (y, out, norm)
+* ``zs_backward_normalized(grad_y, out, norm, coupling, radial, csr)``
+  -> (grad_coupling, grad_radial, grad_env, grad_deg)
 
 plus ``gie_zonal_scatter(coupling, radial, csr)``, an autograd function with
 the operator boundary of deepmd-kit PR #6072 ("fused Triton zonal scatter for
@@ -17,6 +20,9 @@ the GIE head", section "Boundary and layout contract"): only fp32 is
 accepted and no double backward is provided.  Unlike that boundary, strided
 views of the edge inputs are read in place instead of being copied to
 contiguous tensors (``zs_forward_strided`` / ``zs_backward_strided``).
+``gie_zonal_scatter_normalized(coupling, radial, env, csr)`` adds the
+inverse-square-root degree normalisation that follows the scatter on the same
+page ("What", third bullet), with the envelope gradient it carries.
 """
 from __future__ import annotations
 
@@ -69,6 +75,11 @@ def load() -> ctypes.CDLL:
         lib.zs_backward_strided.argtypes = [P, P, I64, P, I64, I64, P, P, P, I64, I64, I64, P, P,
                                             P]
         lib.zs_backward_strided.restype = INT
+        lib.zs_forward_normalized.argtypes = [P, P, P, P, P, I64, I64, I64, P, P, P, P]
+        lib.zs_forward_normalized.restype = INT
+        lib.zs_backward_normalized.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, P, P, P, P,
+                                               P]
+        lib.zs_backward_normalized.restype = INT
         _lib = lib
     return _lib
 
@@ -222,6 +233,61 @@ def zs_backward(grad_out: torch.Tensor, coupling: torch.Tensor, radial: torch.Te
     return grad_coupling, grad_radial
 
 
+def _edge_inputs(coupling, radial):
+    coupling = _dev_tensor(coupling, "coupling", torch.float32)
+    radial = _dev_tensor(radial, "radial", torch.float32)
+    if coupling.dim() != 2 or coupling.shape[1] != ZONAL:
+        raise ValueError("coupling must be (E, 15)")
+    if radial.dim() != 3 or radial.shape[1] != SLOTS or radial.shape[0] != coupling.shape[0]:
+        raise ValueError("radial must be (E, 3, C) with the same E as coupling")
+    return coupling, radial
+
+
+def zs_forward_normalized(coupling: torch.Tensor, radial: torch.Tensor, env: torch.Tensor,
+                          csr: Csr, keep_out: bool = True):
+    """(y, out, norm): y = out * norm[:, None, None] with norm = deg^(-1/2)
+    (0 where deg <= 0) and deg the per-node sum of ``env`` (E,).  ``out`` is
+    the unnormalised scatter (None when ``keep_out`` is False).  Inputs are
+    made contiguous."""
+    coupling, radial = _edge_inputs(coupling, radial)
+    env = _dev_tensor(env, "env", torch.float32)
+    E, C = radial.shape[0], radial.shape[2]
+    if env.shape != (E,):
+        raise ValueError("env must be (E,)")
+    dev = radial.device
+    y = torch.empty((csr.n_nodes, ROWS, C), dtype=torch.float32, device=dev)
+    out = torch.empty_like(y) if keep_out else None
+    norm = torch.empty(csr.n_nodes, dtype=torch.float32, device=dev)
+    _check("zs_forward_normalized", load().zs_forward_normalized(
+        _ptr(coupling), _ptr(radial), _ptr(env), _ptr(csr.rowptr), _ptr(csr.perm), csr.n_nodes,
+        E, C, _ptr(y), _ptr(out), _ptr(norm), _stream()))
+    return y, out, norm
+
+
+def zs_backward_normalized(grad_y: torch.Tensor, out: torch.Tensor, norm: torch.Tensor,
+                           coupling: torch.Tensor, radial: torch.Tensor, csr: Csr):
+    """(grad_coupling (E, 15), grad_radial (E, 3, C), grad_env (E,),
+    grad_deg (N,)) for y = zs_forward_normalized(...)[0]."""
+    coupling, radial = _edge_inputs(coupling, radial)
+    grad_y = _dev_tensor(grad_y, "grad_y", torch.float32)
+    out = _dev_tensor(out, "out", torch.float32)
+    norm = _dev_tensor(norm, "norm", torch.float32)
+    E, C = radial.shape[0], radial.shape[2]
+    N = csr.n_nodes
+    if grad_y.shape != (N, ROWS, C) or out.shape != (N, ROWS, C) or norm.shape != (N,):
+        raise ValueError("grad_y and out must be (N, 16, C), norm (N,)")
+    dev = radial.device
+    gc = torch.empty((E, ZONAL), dtype=torch.float32, device=dev)
+    gr = torch.empty((E, SLOTS, C), dtype=torch.float32, device=dev)
+    ge = torch.empty(E, dtype=torch.float32, device=dev)
+    gd = torch.empty(N, dtype=torch.float32, device=dev)
+    _check("zs_backward_normalized", load().zs_backward_normalized(
+        _ptr(grad_y), _ptr(out), _ptr(norm), _ptr(coupling), _ptr(radial), _ptr(csr.dst32),
+        _ptr(csr.rowptr), _ptr(csr.perm), N, E, C, _ptr(gc), _ptr(gr), _ptr(ge), _ptr(gd),
+        _stream()))
+    return gc, gr, ge, gd
+
+
 class _GieZonalScatter(torch.autograd.Function):
     @staticmethod
     def forward(ctx, coupling, radial, rowptr, perm, dst32, n_nodes):
@@ -244,3 +310,36 @@ def gie_zonal_scatter(coupling: torch.Tensor, radial: torch.Tensor, csr: Csr) ->
     example sliced radial features, or the coupling inside a packed Wigner
     band) are read in place; the gradients are contiguous tensors."""
     return _GieZonalScatter.apply(coupling, radial, csr.rowptr, csr.perm, csr.dst32, csr.n_nodes)
+
+
+class _GieZonalScatterNormalized(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, coupling, radial, env, rowptr, perm, dst32, n_nodes):
+        csr = Csr(rowptr, perm, dst32, n_nodes)
+        coupling, radial = coupling.contiguous(), radial.contiguous()
+        y, out, norm = zs_forward_normalized(coupling, radial, env, csr)
+        ctx.save_for_backward(coupling, radial, out, norm, rowptr, perm, dst32)
+        ctx.n_nodes = n_nodes
+        ctx.mark_non_differentiable(norm)
+        return y, norm
+
+    @staticmethod
+    @torch.autograd.function.once_differentiable
+    def backward(ctx, grad_y, grad_norm):
+        coupling, radial, out, norm, rowptr, perm, dst32 = ctx.saved_tensors
+        csr = Csr(rowptr, perm, dst32, ctx.n_nodes)
+        if grad_y is None:
+            grad_y = torch.zeros_like(out)
+        gc, gr, ge, _ = zs_backward_normalized(grad_y.contiguous(), out, norm, coupling, radial,
+                                               csr)
+        return gc, gr, ge, None, None, None, None
+
+
+def gie_zonal_scatter_normalized(coupling: torch.Tensor, radial: torch.Tensor, env: torch.Tensor,
+                                 csr: Csr) -> tuple[torch.Tensor, torch.Tensor]:
+    """Differentiable scatter followed by the degree normalisation:
+    returns (y, norm), y = scatter * norm[:, None, None], norm = deg^(-1/2)
+    with deg the per-node sum of ``env``.  Gradients flow to coupling, radial
+    and env (norm itself is returned as a non-differentiable by-product)."""
+    return _GieZonalScatterNormalized.apply(coupling, radial, env, csr.rowptr, csr.perm,
+                                            csr.dst32, csr.n_nodes)

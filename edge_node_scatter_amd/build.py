@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libzs.so")
-SOURCES = ["zs_api.hip", "zs_csr.hip", "zs_fwd.hip", "zs_bwd.hip"]
+SOURCES = ["zs_api.hip", "zs_csr.hip", "zs_fwd.hip", "zs_bwd.hip", "zs_norm.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -127,7 +127,8 @@ int forward_impl(const float* coupling, int64_t cs, const float* radial, int64_t
     const bool vec4 = channels % 4 == 0 && aligned(out, 16) &&
                       (n_edges == 0 || (aligned(radial, 16) && re % 4 == 0 && rs % 4 == 0));
     return hip_status(zs::launch_forward(coupling, radial, zs::InLayout{cs, re, rs}, rowptr, perm,
-                                         n_nodes, n_edges, channels, out, vec4, s));
+                                         n_nodes, n_edges, channels, out, vec4,
+                                         zs::NormIO{nullptr, nullptr, nullptr}, s));
 }
 
 int backward_impl(const float* grad_out, const float* coupling, int64_t cs, const float* radial,
@@ -159,7 +160,7 @@ int backward_impl(const float* grad_out, const float* coupling, int64_t cs, cons
                       aligned(grad_radial, 16) && re % 4 == 0 && rs % 4 == 0;
     return hip_status(zs::launch_backward(grad_out, coupling, radial, zs::InLayout{cs, re, rs},
                                           dst32, rowptr, perm, n_nodes, n_edges, channels,
-                                          grad_coupling, grad_radial, vec4, s));
+                                          grad_coupling, grad_radial, vec4, nullptr, s));
 }
 
 }  // namespace
@@ -197,6 +198,85 @@ int zs_backward_strided(const float* grad_out, const float* coupling,
     return backward_impl(grad_out, coupling, coupling_edge_stride, radial, radial_edge_stride,
                          radial_slot_stride, dst32, rowptr, perm, n_nodes, n_edges, channels,
                          grad_coupling, grad_radial, stream);
+}
+
+int zs_forward_normalized(const float* coupling, const float* radial, const float* env,
+                          const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
+                          int64_t n_edges, int64_t channels, float* y, float* out, float* norm,
+                          void* stream) {
+    if (!sizes_ok(n_edges, n_nodes) || !channels_ok(channels)) return ZS_ERR_SHAPE;
+    if (!y || !norm || !rowptr || (n_edges > 0 && (!coupling || !radial || !env || !perm)))
+        return ZS_ERR_NULL;
+    if (!aligned(y, 4) || !aligned(norm, 4) || (out && !aligned(out, 4)) || !aligned(rowptr, 4) ||
+        (n_edges > 0 && (!aligned(coupling, 4) || !aligned(radial, 4) || !aligned(env, 4) ||
+                         !aligned(perm, 4))))
+        return ZS_ERR_UNSUPPORTED;
+    const int64_t node_floats = n_nodes * zs::kRows * channels;
+    const Range outs[] = {span(y, node_floats, 4), span(out, out ? node_floats : 0, 4),
+                          span(norm, n_nodes, 4)};
+    const Range ins[] = {span(coupling, n_edges * zs::kZonal, 4),
+                         span(radial, n_edges * zs::kSlots * channels, 4),
+                         span(env, n_edges, 4), span(rowptr, n_nodes + 1, 4),
+                         span(perm, n_edges, 4)};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return ZS_ERR_ALIAS;
+        for (const Range& in : ins)
+            if (overlap(outs[i], in)) return ZS_ERR_ALIAS;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool vec4 = channels % 4 == 0 && aligned(y, 16) && (!out || aligned(out, 16)) &&
+                      (n_edges == 0 || aligned(radial, 16));
+    return hip_status(zs::launch_forward(coupling, radial,
+                                         zs::InLayout{zs::kZonal, zs::kSlots * channels, channels},
+                                         rowptr, perm, n_nodes, n_edges, channels, out, vec4,
+                                         zs::NormIO{env, y, norm}, s));
+}
+
+int zs_backward_normalized(const float* grad_y, const float* out, const float* norm,
+                           const float* coupling, const float* radial, const int32_t* dst32,
+                           const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
+                           int64_t n_edges, int64_t channels, float* grad_coupling,
+                           float* grad_radial, float* grad_env, float* grad_deg, void* stream) {
+    if (!sizes_ok(n_edges, n_nodes) || !channels_ok(channels)) return ZS_ERR_SHAPE;
+    if (!grad_y || !out || !norm || !grad_deg) return ZS_ERR_NULL;
+    if (n_edges > 0 && (!coupling || !radial || !dst32 || !rowptr || !perm || !grad_coupling ||
+                        !grad_radial || !grad_env))
+        return ZS_ERR_NULL;
+    if (!aligned(grad_y, 4) || !aligned(out, 4) || !aligned(norm, 4) || !aligned(grad_deg, 4))
+        return ZS_ERR_UNSUPPORTED;
+    if (n_edges > 0 &&
+        (!aligned(coupling, 4) || !aligned(radial, 4) || !aligned(dst32, 4) ||
+         !aligned(rowptr, 4) || !aligned(perm, 4) || !aligned(grad_coupling, 4) ||
+         !aligned(grad_radial, 4) || !aligned(grad_env, 4)))
+        return ZS_ERR_UNSUPPORTED;
+    const int64_t node_floats = n_nodes * zs::kRows * channels;
+    const int64_t e_in = n_edges > 0 ? n_edges : 0;
+    const Range outs[] = {span(grad_coupling, e_in * zs::kZonal, 4),
+                          span(grad_radial, e_in * zs::kSlots * channels, 4),
+                          span(grad_env, e_in, 4), span(grad_deg, n_nodes, 4)};
+    const Range ins[] = {span(grad_y, node_floats, 4), span(out, node_floats, 4),
+                         span(norm, n_nodes, 4), span(coupling, e_in * zs::kZonal, 4),
+                         span(radial, e_in * zs::kSlots * channels, 4), span(dst32, e_in, 4),
+                         span(rowptr, n_edges > 0 ? n_nodes + 1 : 0, 4), span(perm, e_in, 4)};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return ZS_ERR_ALIAS;
+        for (const Range& in : ins)
+            if (overlap(outs[i], in)) return ZS_ERR_ALIAS;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (n_edges > 0) {
+        const bool vec4 = channels % 4 == 0 && aligned(grad_y, 16) && aligned(radial, 16) &&
+                          aligned(grad_radial, 16);
+        const hipError_t err = zs::launch_backward(
+            grad_y, coupling, radial, zs::InLayout{zs::kZonal, zs::kSlots * channels, channels},
+            dst32, rowptr, perm, n_nodes, n_edges, channels, grad_coupling, grad_radial, vec4,
+            norm, s);
+        if (err != hipSuccess) return ZS_ERR_HIP;
+    }
+    return hip_status(zs::launch_norm_grad(grad_y, out, norm, dst32, n_nodes, n_edges, channels,
+                                           grad_deg, grad_env, s));
 }
 
 }  // extern "C"

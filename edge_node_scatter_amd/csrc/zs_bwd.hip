@@ -65,7 +65,8 @@ __global__ __launch_bounds__(256) void zs_bwd_kernel(
     const float* __restrict__ grad_out, const float* __restrict__ coupling,
     const float* __restrict__ radial, InLayout L, const int32_t* __restrict__ rowptr,
     const int32_t* __restrict__ perm, int64_t n_nodes, int64_t n_edges, int64_t C,
-    float* __restrict__ grad_coupling, float* __restrict__ grad_radial) {
+    float* __restrict__ grad_coupling, float* __restrict__ grad_radial,
+    const float* __restrict__ norm) {
     using V = VecT<VEC>;
     using VT = typename V::T;
     constexpr int EPW = 64 / NQ;
@@ -88,6 +89,9 @@ __global__ __launch_bounds__(256) void zs_bwd_kernel(
         k1 = k1 < k0 ? k0 : (k1 > n_edges ? n_edges : k1);
         if (k0 >= k1) continue;
         const float* gnode = grad_out + node * kRows * C;
+        // upstream rows are grad_out * norm[node] (fp32) when normalised;
+        // multiplying by 1.0f otherwise leaves them bit-identical
+        const float gs = norm != nullptr ? norm[node] : 1.0f;
 
         float greg[kZonal][VEC];
         if (GREG) {
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(256) void zs_bwd_kernel(
                 VT t{};
                 if (c0 < C) t = V::load(gnode + int64_t(r) * C + c0);
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) greg[r - 1][v] = c0 < C ? V::get(t, v) : 0.0f;
+                for (int v = 0; v < VEC; ++v) greg[r - 1][v] = c0 < C ? V::get(t, v) * gs : 0.0f;
             }
         }
 
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(256) void zs_bwd_kernel(
                         VT tv{};
                         if (act) tv = V::load(gnode + int64_t(r) * C + c0);
 #pragma unroll
-                        for (int v = 0; v < VEC; ++v) g[r - 1][v] = act ? V::get(tv, v) : 0.0f;
+                        for (int v = 0; v < VEC; ++v) g[r - 1][v] = act ? V::get(tv, v) * gs : 0.0f;
                     }
                 }
                 float x[kSlots][VEC];
@@ -398,7 +402,8 @@ void zs_bwd_staged_kernel(
     const float* __restrict__ grad_out, const float* __restrict__ coupling,
     const float* __restrict__ radial, InLayout L, const int32_t* __restrict__ rowptr,
     const int32_t* __restrict__ perm, int64_t n_nodes, int64_t n_edges, int64_t C,
-    float* __restrict__ grad_coupling, float* __restrict__ grad_radial) {
+    float* __restrict__ grad_coupling, float* __restrict__ grad_radial,
+    const float* __restrict__ norm) {
     constexpr int EPW = 64 / NQ;
     __shared__ float4 gsh[kZonal * NQ];
     __shared__ float4 wsh4[EPW * 4];
@@ -417,11 +422,15 @@ void zs_bwd_staged_kernel(
         k1 = k1 < k0 ? k0 : (k1 > n_edges ? n_edges : k1);
         if (k0 >= k1) continue;
         const float* gnode = grad_out + node * kRows * C;
+        const float gs = norm != nullptr ? norm[node] : 1.0f;   // see zs_bwd_kernel
         for (int i = lane; i < kZonal * NQ; i += 64) {
             const int r = i / NQ + 1;
             const int64_t c = int64_t(i % NQ) * 4;
             float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (c < C) v = *reinterpret_cast<const float4*>(gnode + int64_t(r) * C + c);
+            if (c < C) {
+                v = *reinterpret_cast<const float4*>(gnode + int64_t(r) * C + c);
+                v.x = v.x * gs; v.y = v.y * gs; v.z = v.z * gs; v.w = v.w * gs;
+            }
             gsh[i] = v;
         }
         const int64_t nsteps = (k1 - k0 + EPW - 1) / EPW;
@@ -450,18 +459,18 @@ hipError_t launch_backward(const float* grad_out, const float* coupling, const f
                            InLayout L, const int32_t* dst32, const int32_t* rowptr,
                            const int32_t* perm, int64_t n_nodes, int64_t n_edges,
                            int64_t channels, float* grad_coupling, float* grad_radial, bool vec4,
-                           hipStream_t stream) {
+                           const float* norm, hipStream_t stream) {
     (void)dst32;   // this traversal is CSR-major; dst32 serves edge-major variants
     constexpr int64_t kGridCap = 1 << 20;
     const unsigned gx = unsigned(n_nodes < kGridCap ? n_nodes : kGridCap);
 #define ZS_BWD_LAUNCH(VEC, NQ, GREG)                                                            \
     zs_bwd_kernel<VEC, NQ, GREG><<<gx, 256, 0, stream>>>(grad_out, coupling, radial, L, rowptr,  \
                                                          perm, n_nodes, n_edges, channels,       \
-                                                         grad_coupling, grad_radial)
+                                                         grad_coupling, grad_radial, norm)
 #define ZS_BWD_STAGED(NQ, FULL)                                                                  \
     zs_bwd_staged_kernel<NQ, FULL><<<gx, 64, 0, stream>>>(grad_out, coupling, radial, L, rowptr,   \
                                                          perm, n_nodes, n_edges, channels,       \
-                                                         grad_coupling, grad_radial)
+                                                         grad_coupling, grad_radial, norm)
     if (vec4) {
         if (channels == 32)
             ZS_BWD_STAGED(8, true);

@@ -26,13 +26,14 @@ namespace zs {
 
 namespace {
 
-template <int VEC, int NQ, int U>
+// NORM: as zs_fwd_staged_kernel below (envelope sum, y, norm, optional out).
+template <int VEC, int NQ, int U, bool NORM>
 __global__ __launch_bounds__(64) void zs_fwd_kernel(const float* __restrict__ coupling,
                                                     const float* __restrict__ radial, InLayout L,
                                                     const int32_t* __restrict__ rowptr,
                                                     const int32_t* __restrict__ perm,
                                                     int64_t n_nodes, int64_t n_edges, int64_t C,
-                                                    float* __restrict__ out) {
+                                                    float* __restrict__ out, NormIO nio) {
     using V = VecT<VEC>;
     using VT = typename V::T;
     constexpr int NS = 64 / NQ;
@@ -61,6 +62,7 @@ __global__ __launch_bounds__(64) void zs_fwd_kernel(const float* __restrict__ co
         for (int i = 0; i < RPS; ++i)
 #pragma unroll
             for (int v = 0; v < VEC; ++v) acc[i][v] = 0.0f;
+        float deg = 0.0f;
 
         for (int64_t k = k0; k < k1; k += U) {
             int32_t e[U];
@@ -71,6 +73,11 @@ __global__ __launch_bounds__(64) void zs_fwd_kernel(const float* __restrict__ co
             }
             VT xa[U], xb[U];
             float w[U][RPS];
+            float ev[U];
+            if (NORM) {
+#pragma unroll
+                for (int b = 0; b < U; ++b) ev[b] = e[b] >= 0 ? nio.env[e[b]] : 0.0f;
+            }
 #pragma unroll
             for (int b = 0; b < U; ++b) {
                 if (e[b] >= 0 && act) {
@@ -87,6 +94,7 @@ __global__ __launch_bounds__(64) void zs_fwd_kernel(const float* __restrict__ co
             }
 #pragma unroll
             for (int b = 0; b < U; ++b) {
+                if (NORM && e[b] >= 0) deg = deg + ev[b];
                 if (e[b] >= 0 && act) {
 #pragma unroll
                     for (int i = 0; i < RPS; ++i) {
@@ -104,19 +112,25 @@ __global__ __launch_bounds__(64) void zs_fwd_kernel(const float* __restrict__ co
             }
         }
 
-        if (act) {
-            float* onode = out + node * kRows * C + c0;
+        float nrm = 1.0f;
+        if (NORM) {
+            nrm = deg > 0.0f ? 1.0f / sqrtf(deg) : 0.0f;
+            if (lane == 0 && blockIdx.y == 0) nio.norm[node] = nrm;
+        }
+#pragma unroll
+        for (int pass = 0; pass < (NORM ? 2 : 1); ++pass) {
+            // NORM: pass 0 writes y, pass 1 the unnormalised out (if requested)
+            float* base = (NORM && pass == 0) ? nio.y : out;
+            if (!act || base == nullptr) continue;
+            float* onode = base + node * kRows * C + c0;
 #pragma unroll
             for (int i = 0; i < RPS; ++i) {
                 const int r = r_first + i;
-                if (r <= kZonal) {
-                    V::store(onode + int64_t(r) * C, acc[i]);
-                } else {
-                    float z[VEC];
+                float v[VEC];
 #pragma unroll
-                    for (int v = 0; v < VEC; ++v) z[v] = 0.0f;
-                    V::store(onode, z);   // scalar row 0
-                }
+                for (int u = 0; u < VEC; ++u)
+                    v[u] = r > kZonal ? 0.0f : ((NORM && pass == 0) ? acc[i][u] * nrm : acc[i][u]);
+                V::store(r <= kZonal ? onode + int64_t(r) * C : onode, v);   // row 0 is +0
             }
         }
     }
@@ -187,9 +201,13 @@ __device__ __attribute__((always_inline)) inline int perm_resolve(PermRaw p, int
 
 // Loads of one batch, all unconditional: absent edges and channels past C read
 // a valid substitute (edge 0, the tile's first channel) that is never used.
+// With NORM, the fetch slots after the batch's 15 * kFwdBatch coupling floats
+// carry the edges' envelope factors (one per edge).
+template <bool NORM>
 __device__ __attribute__((always_inline)) inline void fwd_fetch(FwdRegs& R, int lane, int pe,
                                                                  const float* __restrict__ coupling,
                                                                  const float* __restrict__ radial,
+                                                                 const float* __restrict__ env,
                                                                  const InLayout& L, int64_t C,
                                                                  int64_t cbase) {
 #pragma unroll
@@ -206,23 +224,32 @@ __device__ __attribute__((always_inline)) inline void fwd_fetch(FwdRegs& R, int 
     for (int i = 0; i < kFwdCplVec; ++i) {
         const int idx = fwd_cpl_idx(i, lane);
         const bool in = idx < kFwdBatch * kZonal;
-        const int e = __shfl(pe, in ? idx / kZonal : 0, 64);
+        const bool in_env = NORM && !in && idx < kFwdBatch * (kZonal + 1);
+        const int b = in ? idx / kZonal : (in_env ? idx - kFwdBatch * kZonal : 0);
+        const int e = __shfl(pe, b, 64);
         const int64_t es = e >= 0 ? e : 0;
-        R.w[i] = coupling[es * L.cpl_edge + (in ? idx % kZonal : 0)];
+        R.w[i] = in_env ? env[es] : coupling[es * L.cpl_edge + (in ? idx % kZonal : 0)];
     }
 }
 
+// With NORM the envelope factor of batch edge b sits in csh[b * 16 + 15] and
+// deg accumulates the envelopes in edge order (fp32 adds from +0).
+template <bool NORM>
 __device__ __attribute__((always_inline)) inline void fwd_stage_accumulate(
     const FwdRegs& R, float4* rsh, float* csh, int cnt, int lane, int q, int j, int sA, int sB,
-    float (&acc0)[4], float (&acc1)[4]) {
+    float (&acc0)[4], float (&acc1)[4], float& deg) {
 #pragma unroll
     for (int i = 0; i < kFwdRadVec; ++i) rsh[i * 64 + lane] = R.r[i];
 #pragma unroll
     for (int i = 0; i < kFwdCplVec; ++i) {
         const int idx = fwd_cpl_idx(i, lane);
-        if (idx < kFwdBatch * kZonal) csh[(idx / kZonal) * 16 + idx % kZonal] = R.w[i];
+        if (idx < kFwdBatch * kZonal)
+            csh[(idx / kZonal) * 16 + idx % kZonal] = R.w[i];
+        else if (NORM && idx < kFwdBatch * (kZonal + 1))
+            csh[(idx - kFwdBatch * kZonal) * 16 + 15] = R.w[i];
     }
     auto edge = [&](int b) {
+        if (NORM) deg = deg + csh[b * 16 + 15];
         const float4 xa = rsh[b * (kSlots * 8) + sA * 8 + q];
         const float4 xb = rsh[b * (kSlots * 8) + sB * 8 + q];
         const float w0 = csh[b * 16 + 2 * j];
@@ -246,13 +273,19 @@ __device__ __attribute__((always_inline)) inline void fwd_stage_accumulate(
     }
 }
 
+// NORM: also accumulate each node's envelope sum deg in edge order and write
+// y = out * norm with norm = 1/sqrt(deg) (0 for deg <= 0); out (the
+// unnormalised sum) is written only when the pointer is non-null.
+template <bool NORM>
 __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restrict__ coupling,
                                                            const float* __restrict__ radial,
                                                            InLayout L,
                                                            const int32_t* __restrict__ rowptr,
                                                            const int32_t* __restrict__ perm,
                                                            int64_t n_nodes, int64_t n_edges,
-                                                           int64_t C, float* __restrict__ out) {
+                                                           int64_t C, float* __restrict__ out,
+                                                           NormIO nio) {
+    static_assert(kFwdCplVec * 64 >= kFwdBatch * (kZonal + 1), "envelope slots");
     __shared__ float4 rsh[kFwdBatch * kSlots * 8];
     __shared__ float csh[kFwdBatch * 16];
 
@@ -277,6 +310,7 @@ __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restri
 
         float acc0[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         float acc1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float deg = 0.0f;
         auto batch_count = [k0, k1](int64_t t) {
             const int64_t kb = k0 + t * kFwdBatch;
             return int(k1 - kb < kFwdBatch ? k1 - kb : kFwdBatch);
@@ -286,22 +320,39 @@ __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restri
             FwdRegs RA, RB;
             PermRaw rA = perm_issue(perm, k0, k1, lane, kFwdBatch);
             PermRaw rB = perm_issue(perm, k0 + kFwdBatch, k1, lane, kFwdBatch);
-            fwd_fetch(RA, lane, perm_resolve(rA, n_edges), coupling, radial, L, C, cbase);
+            fwd_fetch<NORM>(RA, lane, perm_resolve(rA, n_edges), coupling, radial, nio.env, L, C,
+                            cbase);
             for (int64_t t = 0; t < nb; t += 2) {
                 const PermRaw rN = perm_issue(perm, k0 + (t + 2) * kFwdBatch, k1, lane, kFwdBatch);
-                fwd_fetch(RB, lane, perm_resolve(rB, n_edges), coupling, radial, L, C,
-                          cbase);
-                fwd_stage_accumulate(RA, rsh, csh, batch_count(t), lane, q, j, sA, sB, acc0, acc1);
+                fwd_fetch<NORM>(RB, lane, perm_resolve(rB, n_edges), coupling, radial, nio.env, L,
+                                C, cbase);
+                fwd_stage_accumulate<NORM>(RA, rsh, csh, batch_count(t), lane, q, j, sA, sB, acc0,
+                                           acc1, deg);
                 if (t + 1 >= nb) break;
                 rB = perm_issue(perm, k0 + (t + 3) * kFwdBatch, k1, lane, kFwdBatch);
-                fwd_fetch(RA, lane, perm_resolve(rN, n_edges), coupling, radial, L, C,
-                          cbase);
-                fwd_stage_accumulate(RB, rsh, csh, batch_count(t + 1), lane, q, j, sA, sB, acc0,
-                                     acc1);
+                fwd_fetch<NORM>(RA, lane, perm_resolve(rN, n_edges), coupling, radial, nio.env, L,
+                                C, cbase);
+                fwd_stage_accumulate<NORM>(RB, rsh, csh, batch_count(t + 1), lane, q, j, sA, sB,
+                                           acc0, acc1, deg);
             }
         }
 
-        if (act) {
+        if (NORM) {
+            const float nrm = deg > 0.0f ? 1.0f / sqrtf(deg) : 0.0f;
+            if (lane == 0 && blockIdx.y == 0) nio.norm[node] = nrm;
+            if (act) {
+                float* ynode = nio.y + node * kRows * C + c0;
+                float4 v0, v1;
+                v0.x = acc0[0] * nrm; v0.y = acc0[1] * nrm; v0.z = acc0[2] * nrm; v0.w = acc0[3] * nrm;
+                v1.x = acc1[0] * nrm; v1.y = acc1[1] * nrm; v1.z = acc1[2] * nrm; v1.w = acc1[3] * nrm;
+                *reinterpret_cast<float4*>(ynode + int64_t(rA) * C) = v0;
+                if (rA + 1 <= kZonal)
+                    *reinterpret_cast<float4*>(ynode + int64_t(rA + 1) * C) = v1;
+                else
+                    *reinterpret_cast<float4*>(ynode) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+        }
+        if (act && (!NORM || out != nullptr)) {
             float* onode = out + node * kRows * C + c0;
             *reinterpret_cast<float4*>(onode + int64_t(rA) * C) =
                 make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
@@ -319,18 +370,27 @@ __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restri
 hipError_t launch_forward(const float* coupling, const float* radial, InLayout L,
                           const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
                           int64_t n_edges, int64_t channels, float* out, bool vec4,
-                          hipStream_t stream) {
+                          NormIO nio, hipStream_t stream) {
     constexpr int64_t kGridCap = 1 << 20;
     const unsigned gx = unsigned(n_nodes < kGridCap ? n_nodes : kGridCap);
+    const bool norm = nio.y != nullptr;   // env may be NULL when there are no edges
     if (vec4) {
         const unsigned gy = unsigned((channels + 31) / 32);
-        zs_fwd_staged_kernel<<<dim3(gx, gy), 64, 0, stream>>>(coupling, radial, L, rowptr, perm,
-                                                              n_nodes, n_edges, channels, out);
+        if (norm)
+            zs_fwd_staged_kernel<true><<<dim3(gx, gy), 64, 0, stream>>>(
+                coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
+        else
+            zs_fwd_staged_kernel<false><<<dim3(gx, gy), 64, 0, stream>>>(
+                coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
     } else {
         constexpr int NQ = 16, VEC = 1;
         const unsigned gy = unsigned((channels + NQ * VEC - 1) / (NQ * VEC));
-        zs_fwd_kernel<VEC, NQ, 8><<<dim3(gx, gy), 64, 0, stream>>>(
-            coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out);
+        if (norm)
+            zs_fwd_kernel<VEC, NQ, 8, true><<<dim3(gx, gy), 64, 0, stream>>>(
+                coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
+        else
+            zs_fwd_kernel<VEC, NQ, 8, false><<<dim3(gx, gy), 64, 0, stream>>>(
+                coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
     }
     return hipGetLastError();
 }

@@ -98,16 +98,36 @@ struct InLayout {
     int64_t rad_slot;   // radial: slot -> slot
 };
 
+// Inverse-square-root degree normalisation fused into the scatter.  Forward:
+// env [n_edges] is read, y [n_nodes][16][C] = out * norm and norm [n_nodes] are
+// written (out itself only when non-null).  Backward: norm [n_nodes] scales the
+// upstream rows before they are used.  y == nullptr selects the plain scatter
+// (env may be null when there are no edges).
+struct NormIO {
+    const float* env;
+    float* y;
+    float* norm;
+};
+
 hipError_t launch_forward(const float* coupling, const float* radial, InLayout L,
                           const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
                           int64_t n_edges, int64_t channels, float* out, bool vec4,
-                          hipStream_t stream);
+                          NormIO nio, hipStream_t stream);
 
+// norm: null for the plain backward; else grad_out is the gradient of y and is
+// multiplied by norm[dst] (fp32) on load.
 hipError_t launch_backward(const float* grad_out, const float* coupling, const float* radial,
                            InLayout L, const int32_t* dst32, const int32_t* rowptr,
                            const int32_t* perm, int64_t n_nodes, int64_t n_edges,
                            int64_t channels, float* grad_coupling, float* grad_radial, bool vec4,
-                           hipStream_t stream);
+                           const float* norm, hipStream_t stream);
+
+// Envelope gradient of the normalisation: grad_deg[n] (fp32, per node) from
+// grad_y, out and norm, then grad_env[e] = grad_deg[dst32[e]] (0 for dst32 < 0).
+hipError_t launch_norm_grad(const float* grad_y, const float* out, const float* norm,
+                            const int32_t* dst32, int64_t n_nodes, int64_t n_edges,
+                            int64_t channels, float* grad_deg, float* grad_env,
+                            hipStream_t stream);
 
 // Small fill kernel (used instead of hipMemsetAsync so the calls stay
 // capturable in HIP graphs).

@@ -178,6 +178,62 @@ int zs_backward_strided(const float *grad_out, const float *coupling,
                         int64_t channels, float *grad_coupling,
                         float *grad_radial, void *stream);
 
+/*
+ * zs_forward_normalized -- the scatter followed by the inverse-square-root
+ * degree normalisation the GIE page keeps after it ("What", third bullet; last
+ * step of the sequence diagram), fused into the same node-parallel pass.  The
+ * degree is the sum of the edges' cutoff-envelope factors.
+ *
+ *   coupling, radial, rowptr, perm, n_nodes, n_edges, channels  as in zs_forward
+ *   env   [n_edges]                  fp32  cutoff-envelope factor per edge (input)
+ *   y     [n_nodes][16][channels]    fp32  normalised output (output)
+ *   out   [n_nodes][16][channels]    fp32  unnormalised scatter, bitwise the
+ *                                          zs_forward result (output; may be
+ *                                          NULL when not needed)
+ *   norm  [n_nodes]                  fp32  per-node factor (output)
+ *
+ * deg[n] = fp32 sum of env over the node's edges in increasing edge id, from +0;
+ * norm[n] = 1 / sqrt(deg[n]) (correctly rounded fp32 square root, then fp32
+ * division), or 0 when deg[n] <= 0 (no edges, or NaN);
+ * y[n][r][c] = out[n][r][c] * norm[n] (fp32).  Inputs must be contiguous; the
+ * outputs must not overlap each other or any input.  Run-to-run deterministic.
+ */
+int zs_forward_normalized(const float *coupling, const float *radial,
+                          const float *env, const int32_t *rowptr,
+                          const int32_t *perm, int64_t n_nodes, int64_t n_edges,
+                          int64_t channels, float *y, float *out, float *norm,
+                          void *stream);
+
+/*
+ * zs_backward_normalized -- gradients through the normalised scatter (same
+ * page and passage: the normalisation keeps its own cotangent because the
+ * degree depends on geometry through the envelope).
+ *
+ *   grad_y  [n_nodes][16][channels]  fp32  upstream gradient of y (row 0 unused)
+ *   out, norm                              from zs_forward_normalized (inputs)
+ *   coupling, radial, dst32, rowptr, perm  as in zs_backward
+ *   grad_coupling, grad_radial             as in zs_backward, computed with
+ *                                          grad_out[n][r][c] = fp32(grad_y *
+ *                                          norm[n]) (outputs)
+ *   grad_env [n_edges]  fp32  gradient of env (output)
+ *   grad_deg [n_nodes]  fp32  gradient of deg (output; also the per-node table
+ *                             grad_env is gathered from)
+ *
+ * grad_deg[n] = -1/2 * t * t * t * s, t = norm[n], evaluated in fp64 from the
+ * left, s = sum over rows 1..15 and channels of grad_y * out (exact products,
+ * fp64 sum), rounded to fp32 once; 0 when norm[n] == 0.
+ * grad_env[e] = grad_deg[dst32[e]] (0 where dst32[e] < 0).  When n_edges == 0
+ * only grad_deg is written and the edge pointers may be NULL.  Inputs must be
+ * contiguous; outputs must not overlap each other or any input.
+ */
+int zs_backward_normalized(const float *grad_y, const float *out,
+                           const float *norm, const float *coupling,
+                           const float *radial, const int32_t *dst32,
+                           const int32_t *rowptr, const int32_t *perm,
+                           int64_t n_nodes, int64_t n_edges, int64_t channels,
+                           float *grad_coupling, float *grad_radial,
+                           float *grad_env, float *grad_deg, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,8 @@ def test_header_symbols_exported(lib):
     declared = zs.declared_symbols()
     assert set(declared) == {"zs_status_string", "zs_csr_workspace_bytes", "zs_build_csr",
                              "zs_forward", "zs_backward", "zs_forward_strided",
-                             "zs_backward_strided"}
+                             "zs_backward_strided", "zs_forward_normalized",
+                             "zs_backward_normalized"}
     out = subprocess.check_output(["nm", "-D", "--defined-only", zs.LIB_PATH], text=True)
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for name in declared:
@@ -111,6 +112,48 @@ def test_strided_rejects(lib):
     assert b(A, B, 46, C_, 160, 32, D, D + 4096, D + 8192, 4, 10, 32, W, C_ + 4 * 1500,
              None) == ZS_ERR_ALIAS
     assert b(A, B, 46, C_, 160, 32, D, D + 4096, D + 8192, 4, 0, 32, W, X, None) == 0
+
+
+def test_normalized_rejects(lib):
+    # zs_forward_normalized(coupling, radial, env, rowptr, perm, N, E, C, y, out, norm, stream)
+    f = lib.zs_forward_normalized
+    Y, O, NR = X, X + (1 << 20), X + (2 << 20)
+    assert f(A, B, W, C_, D, 4, 10, 0, Y, O, NR, None) == ZS_ERR_SHAPE
+    assert f(A, B, None, C_, D, 4, 10, 32, Y, O, NR, None) == ZS_ERR_NULL      # env
+    assert f(A, B, W, C_, D, 4, 10, 32, Y, O, None, None) == ZS_ERR_NULL      # norm
+    assert f(A, B, W, C_, D, 4, 10, 32, None, O, NR, None) == ZS_ERR_NULL     # y
+    assert f(A, B, W + 2, C_, D, 4, 10, 32, Y, O, NR, None) == ZS_ERR_UNSUPPORTED
+    assert f(A, B, W, C_, D, 4, 10, 32, Y, O + 1, NR, None) == ZS_ERR_UNSUPPORTED
+    assert f(A, B, W, C_, D, 4, 10, 32, Y, Y + 64, NR, None) == ZS_ERR_ALIAS  # out over y
+    assert f(A, B, W, C_, D, 4, 10, 32, Y, O, O + 8, None) == ZS_ERR_ALIAS    # norm over out
+    assert f(A, B, W, C_, D, 4, 10, 32, Y, None, Y + 4, None) == ZS_ERR_ALIAS  # norm over y
+    assert f(A, B, W, C_, D, 4, 10, 32, Y, O, W + 4, None) == ZS_ERR_ALIAS    # norm over env
+    assert f(A, B, W, C_, D, 4, 10, 32, B + 64, O, NR, None) == ZS_ERR_ALIAS  # y over radial
+    # zs_backward_normalized(gy, out, norm, coupling, radial, dst32, rowptr, perm, N, E, C,
+    #                        gc, gr, genv, gdeg, stream)
+    b = lib.zs_backward_normalized
+    GY, OU, NM = A, A + (1 << 20), A + (2 << 20)
+    GC, GR, GE, GD = X, X + (1 << 20), X + (2 << 20), X + (3 << 20)
+    args = [GY, OU, NM, B, C_, D, D + 4096, D + 8192, 4, 10, 32, GC, GR, GE, GD, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["gy", "out", "norm", "cpl", "rad", "dst32", "rowptr", "perm", "N", "E", "C",
+                 "gc", "gr", "ge", "gd", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return b(*a)
+    assert call(C=0) == ZS_ERR_SHAPE
+    assert call(E=-1) == ZS_ERR_SHAPE
+    assert call(gd=None) == ZS_ERR_NULL
+    assert call(out=None) == ZS_ERR_NULL
+    assert call(ge=None) == ZS_ERR_NULL
+    assert call(gd=GD + 2) == ZS_ERR_UNSUPPORTED
+    assert call(ge=GE + 1) == ZS_ERR_UNSUPPORTED
+    assert call(ge=GC + 8) == ZS_ERR_ALIAS          # grad_env inside grad_coupling
+    assert call(gd=OU + 16) == ZS_ERR_ALIAS         # grad_deg over out
+    assert call(gr=GY) == ZS_ERR_ALIAS              # grad_radial over grad_y
+    assert call(gc=NM) == ZS_ERR_ALIAS              # grad_coupling over norm
 
 
 def test_band_view_helper():
