@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
     "fwd": ["zs_fwd.hip", "zs_internal.h"],
     "bwd": ["zs_bwd.hip", "zs_internal.h"],
     "csr": ["zs_csr.hip", "zs_internal.h"],
+    "norm": ["zs_norm.hip", "zs_internal.h"],
 }
 
 
@@ -64,6 +65,21 @@ def algorithmic_bytes(n_edges: int, n_nodes: int, channels: int) -> dict:
     return {"fwd": fwd, "bwd": bwd, "build": build}
 
 
+def algorithmic_bytes_normalized(n_edges: int, n_nodes: int, channels: int) -> dict:
+    """Unique bytes of the calls with the fused degree normalisation.
+
+    forward : the plain forward's bytes + env 4 per edge + y 16*C*4 and
+              norm 4 per node (out is still written: the backward needs it)
+    backward: the plain backward's bytes (grad_y takes grad_out's place) +
+              per node out rows 1..15 (15*C*4), norm 4 and grad_deg 4; per edge
+              dst32 4 and grad_env 4
+    """
+    E, N, C = n_edges, n_nodes, channels
+    b = algorithmic_bytes(E, N, C)
+    return {"fwd": b["fwd"] + 4 * E + N * (16 * C * 4 + 4),
+            "bwd": b["bwd"] + N * (15 * C * 4 + 8) + 8 * E}
+
+
 def kernel_source_hash(family: str | None = None) -> str:
     """Hash of the sources (and build flags) of one kernel family, or of all."""
     files = sorted({f for fam, fs in KERNEL_SOURCES.items() if family in (None, fam) for f in fs})
@@ -75,7 +91,10 @@ def kernel_source_hash(family: str | None = None) -> str:
 
 
 def _family(kernel: str) -> str:
-    return "fwd" if "fwd" in kernel else ("bwd" if "bwd" in kernel else "csr")
+    for fam in ("fwd", "bwd", "norm"):
+        if fam in kernel:
+            return fam
+    return "csr"
 
 
 def load_traffic(kernel: str, n_calls_per_step: int = 1):
@@ -168,6 +187,35 @@ def cpu_baseline(x, w, budget_s: float = 12.0) -> dict:
                    f"median {med * 1e3:.1f} ms per pass, single thread of "
                    f"{os.cpu_count()} visible"),
     }
+
+
+def time_normalized(zs, torch, cpl, rad, x, csr, dev, steps: int) -> dict:
+    """The same frame through the fused degree normalisation
+    (zs_forward_normalized + zs_backward_normalized, CSR reused), timed with
+    per-call events like the main steps, after the main timed region."""
+    E, N, C = rad.shape[0], csr.n_nodes, rad.shape[2]
+    cpl, rad = cpl.contiguous(), rad.contiguous()
+    env = torch.from_numpy(x["env"]).to(dev)
+    gy = torch.from_numpy(x["grad_out"]).to(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(-3, steps):
+        if i >= 0:
+            evs[i][0].record()
+        y, out, norm = zs.zs_forward_normalized(cpl, rad, env, csr)
+        if i >= 0:
+            evs[i][1].record()
+        zs.zs_backward_normalized(gy, out, norm, cpl, rad, csr)
+        if i >= 0:
+            evs[i][2].record()
+    torch.cuda.synchronize()
+    fwd_us = statistics.fmean(e[0].elapsed_time(e[1]) for e in evs) * 1e3
+    bwd_us = statistics.fmean(e[1].elapsed_time(e[2]) for e in evs) * 1e3
+    nb = algorithmic_bytes_normalized(E, N, C)
+    gbs = (nb["fwd"] + nb["bwd"]) / ((fwd_us + bwd_us) * 1e-6) / 1e9
+    return {"fwd_us": round(fwd_us, 2), "bwd_us": round(bwd_us, 2),
+            "fwd_bwd_us": round(fwd_us + bwd_us, 2), "gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nb,
+            "note": "bwd_us covers the scatter backward and the two degree-gradient kernels"}
 
 
 def main() -> int:
@@ -304,6 +352,7 @@ def main() -> int:
         },
         "source_hash": {fam: kernel_source_hash(fam) for fam in KERNEL_SOURCES},
     }
+    rec["normalized"] = time_normalized(zs, torch, cpl, rad, x, csr, dev, args.steps)
     if args.calibrate_copy:
         src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst_copy = torch.empty_like(src)
