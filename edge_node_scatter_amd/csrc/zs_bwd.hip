@@ -190,15 +190,16 @@ __global__ __launch_bounds__(256) void zs_bwd_kernel(
 
 
 // ---------------------------------------------------------------------------
-// Staged backward for C <= 4*NQ, C % 4 == 0, 16-byte aligned grad_out, radial
-// and grad_radial.  One wavefront per node; lane = b*NQ + q handles channels
-// 4q..4q+3 of edge slot b (EPW = 64/NQ edges per step).
+// Staged backward for C % 4 == 0 with 16-byte aligned grad_out, radial and
+// grad_radial, and C <= NQ*VEC with VEC dividing C.  One wavefront per node;
+// lane = b*NQ + q handles channels q*VEC .. q*VEC+VEC-1 of edge slot b
+// (EPW = 64/NQ edges per step); lanes with q*VEC >= C hold no channels.
 //
 //  - The node's upstream rows g[n][1..15] are staged in LDS once and re-read
 //    every step (holding them and their fp64 conversions in registers across
 //    steps would need ~180 registers).
-//  - Each step's perm entries are fetched two steps ahead; its radial float4s
-//    (three per lane) and its coupling rows (EPW x 15 floats, fetched with
+//  - Each step's perm entries are fetched two steps ahead; its radial values
+//    (3 x VEC per lane) and its coupling rows (EPW x 15 floats, fetched with
 //    coalesced all-distinct loads, at most two per lane) one step ahead into
 //    one of two register buffers, so loads overlap the previous step's math.
 //    Every load is unconditional (absent edges read a valid substitute) so the
@@ -211,11 +212,11 @@ __global__ __launch_bounds__(256) void zs_bwd_kernel(
 //    edge group.
 // Arithmetic is that of zs_bwd_kernel.
 // ---------------------------------------------------------------------------
-template <int NQ>
+template <int NQ, int VEC>
 struct BwdRegs {
     static constexpr int EPW = 64 / NQ;
     static constexpr int CPL = (EPW * kZonal + 63) / 64;   // coupling floats per lane
-    float4 x[kSlots];
+    float x[kSlots][VEC];
     float w[CPL];
 };
 
@@ -239,23 +240,99 @@ __device__ __attribute__((always_inline)) inline int bwd_perm_resolve(PermRaw p,
     return (p.valid && p.raw >= 0 && p.raw < n_edges) ? p.raw : -1;
 }
 
-// Loads of one step, all unconditional: absent edges read edge 0 and channels
-// past C read channel 0; such values are zeroed (channels) or never stored
-// (edges), so they cannot reach a result.
-template <int NQ>
-__device__ __attribute__((always_inline)) inline void bwd_fetch(BwdRegs<NQ>& R, int e, int lane,
-                                                                 bool cact, int64_t c0,
+// VEC consecutive read-once floats (radial) with the widest accesses their
+// alignment allows; q*VEC floats into 16-byte aligned rows.
+template <int VEC, bool NT>
+__device__ __attribute__((always_inline)) inline void load_stream_vec(const float* p,
+                                                                     float (&v)[VEC]) {
+    if constexpr (VEC % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i) {
+            const float4 t = load_stream4<NT>(p + 4 * i);
+            v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+        }
+    } else if constexpr (VEC % 2 == 0) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i) {
+            const f2 t = NT ? __builtin_nontemporal_load(reinterpret_cast<const f2*>(p) + i)
+                            : reinterpret_cast<const f2*>(p)[i];
+            v[2 * i] = t.x; v[2 * i + 1] = t.y;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) v[i] = NT ? __builtin_nontemporal_load(p + i) : p[i];
+    }
+}
+
+template <int VEC, bool NT>
+__device__ __attribute__((always_inline)) inline void store_stream_vec(float* p,
+                                                                      const float (&v)[VEC]) {
+    if constexpr (VEC % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i)
+            store_stream4<NT>(p + 4 * i, make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2],
+                                                     v[4 * i + 3]));
+    } else if constexpr (VEC % 2 == 0) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i) {
+            f2 t = {v[2 * i], v[2 * i + 1]};
+            if (NT)
+                __builtin_nontemporal_store(t, reinterpret_cast<f2*>(p) + i);
+            else
+                reinterpret_cast<f2*>(p)[i] = t;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            if (NT)
+                __builtin_nontemporal_store(v[i], p + i);
+            else
+                p[i] = v[i];
+        }
+    }
+}
+
+template <int VEC>
+__device__ __attribute__((always_inline)) inline void lds_read_vec(const float* p,
+                                                                  float (&v)[VEC]) {
+    if constexpr (VEC % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i) {
+            const float4 t = reinterpret_cast<const float4*>(p)[i];
+            v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+        }
+    } else if constexpr (VEC % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i) {
+            const float2 t = reinterpret_cast<const float2*>(p)[i];
+            v[2 * i] = t.x; v[2 * i + 1] = t.y;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) v[i] = p[i];
+    }
+}
+
+// Loads of one step, all unconditional: absent edges read edge 0 and lanes
+// without channels read channel 0; such values are zeroed (channels) or never
+// stored (edges), so they cannot reach a result.
+template <int NQ, int VEC>
+__device__ __attribute__((always_inline)) inline void bwd_fetch(BwdRegs<NQ, VEC>& R, int e,
+                                                                 int lane, bool cact, int64_t c0,
                                                                  const float* __restrict__ coupling,
                                                                  const float* __restrict__ radial,
                                                                  const InLayout& L) {
-    constexpr int EPW = BwdRegs<NQ>::EPW;
+    constexpr int EPW = BwdRegs<NQ, VEC>::EPW;
     const int64_t es = e >= 0 ? e : 0;
     const int64_t cs = cact ? c0 : 0;
 #pragma unroll
     for (int s = 0; s < kSlots; ++s)
-        R.x[s] = load_stream4<ZS_BWD_NT != 0>(radial + es * L.rad_edge + s * L.rad_slot + cs);
+        load_stream_vec<VEC, ZS_BWD_NT != 0>(radial + es * L.rad_edge + s * L.rad_slot + cs,
+                                             R.x[s]);
 #pragma unroll
-    for (int i = 0; i < BwdRegs<NQ>::CPL; ++i) {
+    for (int i = 0; i < BwdRegs<NQ, VEC>::CPL; ++i) {
         const int idx = i * 64 + lane;               // coupling float of this step
         const bool in = idx < EPW * kZonal;
         const int owner = (in ? idx / kZonal : 0) * NQ;   // a lane of that edge slot
@@ -263,10 +340,6 @@ __device__ __attribute__((always_inline)) inline void bwd_fetch(BwdRegs<NQ>& R, 
         const int64_t ees = ee >= 0 ? ee : 0;
         R.w[i] = coupling[ees * L.cpl_edge + (in ? idx % kZonal : 0)];
     }
-}
-
-__device__ __attribute__((always_inline)) inline float comp(const float4& v, int i) {
-    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
 // Lane exchange of a double inside a 16-lane DPP row.
@@ -321,15 +394,17 @@ __device__ __attribute__((always_inline)) inline double reduce8(double (&v)[8], 
     }
 }
 
-template <int NQ, bool FULL>
+// gsh: the node's upstream rows 1..15, T = NQ*VEC floats each (zero past C).
+template <int NQ, int VEC, bool FULL>
 __device__ __attribute__((always_inline)) inline void bwd_compute(
-    const BwdRegs<NQ>& R, int e, int lane, int b, bool cact, int64_t c0, int q,
-    const float4* gsh, float* wsh, int64_t C, float* __restrict__ grad_coupling,
+    const BwdRegs<NQ, VEC>& R, int e, int lane, int b, bool cact, int64_t c0, int q,
+    const float* gsh, float* wsh, int64_t C, float* __restrict__ grad_coupling,
     float* __restrict__ grad_radial) {
-    constexpr int EPW = BwdRegs<NQ>::EPW;
+    constexpr int EPW = BwdRegs<NQ, VEC>::EPW;
+    constexpr int T = NQ * VEC;
     // stage this step's coupling rows, then read the 15 weights of edge slot b
 #pragma unroll
-    for (int i = 0; i < BwdRegs<NQ>::CPL; ++i) {
+    for (int i = 0; i < BwdRegs<NQ, VEC>::CPL; ++i) {
         const int idx = i * 64 + lane;
         if (idx < EPW * kZonal) wsh[(idx / kZonal) * 16 + idx % kZonal] = R.w[i];
     }
@@ -342,10 +417,11 @@ __device__ __attribute__((always_inline)) inline void bwd_compute(
     const bool ok = e >= 0;
     const bool act = ok && cact;
     const int64_t row_stride = int64_t(kSlots) * C;
-    float4 x[kSlots];   // lanes past C contribute exact zeros to the channel sums
+    float x[kSlots][VEC];   // lanes without channels contribute exact zeros to the channel sums
 #pragma unroll
     for (int s = 0; s < kSlots; ++s)
-        x[s] = (FULL || cact) ? R.x[s] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) x[s][v] = (FULL || cact) ? R.x[s][v] : 0.0f;
     float* grow = grad_radial + int64_t(ok ? e : 0) * row_stride + c0;
     float* gcrow = grad_coupling + int64_t(ok ? e : 0) * kZonal;
 #pragma unroll
@@ -357,29 +433,28 @@ __device__ __attribute__((always_inline)) inline void bwd_compute(
         double part[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) part[i] = 0.0;
-        float acc[kSlots][4];
+        float acc[kSlots][VEC];
 #pragma unroll
         for (int s = 0; s < kSlots; ++s)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[s][v] = 0.0f;
+            for (int v = 0; v < VEC; ++v) acc[s][v] = 0.0f;
 #pragma unroll
         for (int r = r_lo; r <= r_hi; ++r) {
-            const float4 g = gsh[(r - 1) * NQ + q];
+            float g[VEC];
+            lds_read_vec<VEC>(gsh + (r - 1) * T + q * VEC, g);
             const int s = row_slot(r);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float p = comp(g, v) * w[r - 1];
+            for (int v = 0; v < VEC; ++v) {
+                const float p = g[v] * w[r - 1];
                 acc[s][v] = acc[s][v] + p;
-                part[r - r_lo] = __builtin_fma(double(comp(g, v)), double(comp(x[s], v)),
-                                               part[r - r_lo]);
+                part[r - r_lo] = __builtin_fma(double(g[v]), double(x[s][v]), part[r - r_lo]);
             }
         }
         if (act) {
 #pragma unroll
             for (int s = 0; s < kSlots; ++s)
                 if (row_slot(r_lo) <= s && s <= row_slot(r_hi))
-                    store_stream4<ZS_BWD_NT != 0>(grow + s * C,
-                                  make_float4(acc[s][0], acc[s][1], acc[s][2], acc[s][3]));
+                    store_stream_vec<VEC, ZS_BWD_NT != 0>(grow + s * C, acc[s]);
         }
         int base;
         const double sum = reduce8<NQ>(part, q, base);
@@ -389,15 +464,20 @@ __device__ __attribute__((always_inline)) inline void bwd_compute(
 }
 
 // Occupancy request for the staged backward: 4 wavefronts per SIMD (<= 128
-// VGPRs) when every lane holds real channels; the masked variants need a few
-// more registers and are left to the compiler (3 per SIMD) rather than spill.
+// VGPRs) for the common shapes whose registers fit; the others are left to
+// the compiler rather than spill.
 #ifndef ZS_BWD_WAVES_PER_EU
 #define ZS_BWD_WAVES_PER_EU 4
 #endif
 
-// FULL: C == 4*NQ, every lane holds real channels (no channel masking).
-template <int NQ, bool FULL>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FULL ? ZS_BWD_WAVES_PER_EU : 1)))
+template <int NQ, int VEC, bool FULL>
+struct BwdOccupancy {
+    static constexpr int v = (FULL && VEC <= 4) ? ZS_BWD_WAVES_PER_EU : 1;
+};
+
+// FULL: C == NQ*VEC, every lane holds real channels (no channel masking).
+template <int NQ, int VEC, bool FULL>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BwdOccupancy<NQ, VEC, FULL>::v)))
 void zs_bwd_staged_kernel(
     const float* __restrict__ grad_out, const float* __restrict__ coupling,
     const float* __restrict__ radial, InLayout L, const int32_t* __restrict__ rowptr,
@@ -405,13 +485,16 @@ void zs_bwd_staged_kernel(
     float* __restrict__ grad_coupling, float* __restrict__ grad_radial,
     const float* __restrict__ norm) {
     constexpr int EPW = 64 / NQ;
-    __shared__ float4 gsh[kZonal * NQ];
+    constexpr int T = NQ * VEC;
+    static_assert(T % 4 == 0, "the upstream rows are staged as float4");
+    __shared__ float4 gsh4[kZonal * T / 4];
     __shared__ float4 wsh4[EPW * 4];
+    float* gsh = reinterpret_cast<float*>(gsh4);
     float* wsh = reinterpret_cast<float*>(wsh4);
     const int lane = threadIdx.x;
     const int q = lane % NQ;
     const int b = lane / NQ;
-    const int64_t c0 = int64_t(q) * 4;
+    const int64_t c0 = int64_t(q) * VEC;
     const bool cact = FULL || c0 < C;
     if (lane < EPW) wsh[lane * 16 + 15] = 0.0f;     // pad column, never fetched
 
@@ -423,34 +506,59 @@ void zs_bwd_staged_kernel(
         if (k0 >= k1) continue;
         const float* gnode = grad_out + node * kRows * C;
         const float gs = norm != nullptr ? norm[node] : 1.0f;   // see zs_bwd_kernel
-        for (int i = lane; i < kZonal * NQ; i += 64) {
-            const int r = i / NQ + 1;
-            const int64_t c = int64_t(i % NQ) * 4;
+        for (int i = lane; i < kZonal * T / 4; i += 64) {
+            const int r = i / (T / 4) + 1;
+            const int64_t c = int64_t(i % (T / 4)) * 4;
             float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             if (c < C) {
                 v = *reinterpret_cast<const float4*>(gnode + int64_t(r) * C + c);
                 v.x = v.x * gs; v.y = v.y * gs; v.z = v.z * gs; v.w = v.w * gs;
             }
-            gsh[i] = v;
+            gsh4[i] = v;
         }
         const int64_t nsteps = (k1 - k0 + EPW - 1) / EPW;
-        BwdRegs<NQ> A, B;
+        BwdRegs<NQ, VEC> A, B;
         const PermRaw qA = bwd_perm_issue(perm, k0 + b, k1);
         PermRaw qB = bwd_perm_issue(perm, k0 + EPW + b, k1);
         int eA = bwd_perm_resolve(qA, n_edges);
-        bwd_fetch<NQ>(A, eA, lane, cact, c0, coupling, radial, L);
+        bwd_fetch<NQ, VEC>(A, eA, lane, cact, c0, coupling, radial, L);
         for (int64_t t = 0; t < nsteps; t += 2) {
             const PermRaw qN = bwd_perm_issue(perm, k0 + (t + 2) * EPW + b, k1);
             const int eB = bwd_perm_resolve(qB, n_edges);
-            bwd_fetch<NQ>(B, eB, lane, cact, c0, coupling, radial, L);
-            bwd_compute<NQ, FULL>(A, eA, lane, b, cact, c0, q, gsh, wsh, C, grad_coupling, grad_radial);
+            bwd_fetch<NQ, VEC>(B, eB, lane, cact, c0, coupling, radial, L);
+            bwd_compute<NQ, VEC, FULL>(A, eA, lane, b, cact, c0, q, gsh, wsh, C, grad_coupling,
+                                       grad_radial);
             if (t + 1 >= nsteps) break;
             qB = bwd_perm_issue(perm, k0 + (t + 3) * EPW + b, k1);
             eA = bwd_perm_resolve(qN, n_edges);
-            bwd_fetch<NQ>(A, eA, lane, cact, c0, coupling, radial, L);
-            bwd_compute<NQ, FULL>(B, eB, lane, b, cact, c0, q, gsh, wsh, C, grad_coupling, grad_radial);
+            bwd_fetch<NQ, VEC>(A, eA, lane, cact, c0, coupling, radial, L);
+            bwd_compute<NQ, VEC, FULL>(B, eB, lane, b, cact, c0, q, gsh, wsh, C, grad_coupling,
+                                       grad_radial);
         }
     }
+}
+
+// Lane layout of the staged backward for a channel count (C % 4 == 0):
+// NQ lanes per edge and VEC channels per lane with VEC dividing C, so every
+// lane holds all or none of its channels.  Layouts with at most 4 channels
+// per lane come first (8 lanes per edge, then 16): wider lanes need more than
+// 128 registers, and the lower occupancy costs more than idle lanes do.
+// Returns false when C needs more than 16 lanes of at most 8 channels.
+bool backward_layout(int64_t C, int& nq, int& vec) {
+    for (int n : {8, 16})
+        for (int v = 1; v <= 4; ++v)
+            if (n * v >= C && C % v == 0) {
+                nq = n;
+                vec = v;
+                return true;
+            }
+    for (int v = 5; v <= 8; ++v)
+        if (16 * v >= C && C % v == 0) {
+            nq = 16;
+            vec = v;
+            return true;
+        }
+    return false;
 }
 
 }  // namespace
@@ -467,21 +575,33 @@ hipError_t launch_backward(const float* grad_out, const float* coupling, const f
     zs_bwd_kernel<VEC, NQ, GREG><<<gx, 256, 0, stream>>>(grad_out, coupling, radial, L, rowptr,  \
                                                          perm, n_nodes, n_edges, channels,       \
                                                          grad_coupling, grad_radial, norm)
-#define ZS_BWD_STAGED(NQ, FULL)                                                                  \
-    zs_bwd_staged_kernel<NQ, FULL><<<gx, 64, 0, stream>>>(grad_out, coupling, radial, L, rowptr,   \
-                                                         perm, n_nodes, n_edges, channels,       \
-                                                         grad_coupling, grad_radial, norm)
-    if (vec4) {
-        if (channels == 32)
-            ZS_BWD_STAGED(8, true);
-        else if (channels < 32)
-            ZS_BWD_STAGED(8, false);
-        else if (channels == 64)
-            ZS_BWD_STAGED(16, true);
-        else if (channels < 64)
-            ZS_BWD_STAGED(16, false);
-        else
-            ZS_BWD_LAUNCH(4, 16, false);
+#define ZS_BWD_STAGED(NQ, VEC)                                                                  \
+    do {                                                                                         \
+        if (channels == (NQ) * (VEC))                                                            \
+            zs_bwd_staged_kernel<NQ, VEC, true><<<gx, 64, 0, stream>>>(                          \
+                grad_out, coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels,         \
+                grad_coupling, grad_radial, norm);                                               \
+        else                                                                                     \
+            zs_bwd_staged_kernel<NQ, VEC, false><<<gx, 64, 0, stream>>>(                         \
+                grad_out, coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels,         \
+                grad_coupling, grad_radial, norm);                                               \
+    } while (0)
+    int nq = 0, vec = 0;
+    if (vec4 && backward_layout(channels, nq, vec)) {
+        switch (nq * 16 + vec) {
+            case 8 * 16 + 1: ZS_BWD_STAGED(8, 1); break;
+            case 8 * 16 + 2: ZS_BWD_STAGED(8, 2); break;
+            case 8 * 16 + 3: ZS_BWD_STAGED(8, 3); break;
+            case 8 * 16 + 4: ZS_BWD_STAGED(8, 4); break;
+            case 16 * 16 + 3: ZS_BWD_STAGED(16, 3); break;
+            case 16 * 16 + 4: ZS_BWD_STAGED(16, 4); break;
+            case 16 * 16 + 5: ZS_BWD_STAGED(16, 5); break;
+            case 16 * 16 + 6: ZS_BWD_STAGED(16, 6); break;
+            case 16 * 16 + 7: ZS_BWD_STAGED(16, 7); break;
+            default: ZS_BWD_STAGED(16, 8); break;
+        }
+    } else if (vec4) {
+        ZS_BWD_LAUNCH(4, 16, false);
     } else {
         if (channels <= 16)
             ZS_BWD_LAUNCH(1, 16, true);

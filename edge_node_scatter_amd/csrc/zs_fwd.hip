@@ -140,42 +140,35 @@ __global__ __launch_bounds__(64) void zs_fwd_kernel(const float* __restrict__ co
 // ---------------------------------------------------------------------------
 // Staged forward for C % 4 == 0 with 16-byte aligned radial and out.
 //
-// Same lane mapping as above with VEC = 4, NQ = 8 (lane = j*8 + q: rows 2j+1,
-// 2j+2 and channels 4q..4q+3 of a 32-channel tile).  The edges of a node are
-// taken 16 at a time (a batch).  A batch's radial rows (16 x 3 x 32 floats)
-// and coupling rows (16 x 15 floats) are fetched with coalesced, all-distinct
-// 16-byte / 4-byte loads (six float4 and up to four floats per lane), kept in
-// registers while the previous batch is being accumulated, then written to
-// LDS from where each lane reads the float4 and two weights it needs per edge.
+// One 64-lane wavefront per (node, channel tile of T = 8*VEC channels);
+// lane = j*8 + q owns padded rows 2j+1, 2j+2 (the one past row 15 stands for
+// row 0) and channels q*VEC .. q*VEC+VEC-1 of the tile, so one wavefront
+// covers up to 64 channels and the node's perm entries and coupling rows are
+// read once per tile.  The edges of a node are taken B at a time (a batch).
+// A batch's radial rows (B x 3 x T floats) and coupling rows (B x 15 floats,
+// plus B envelope factors when normalising) are fetched with coalesced,
+// all-distinct 16-byte / 4-byte loads, kept in registers while the previous
+// batch is accumulated, then written to LDS, from where each lane reads the
+// VEC values of each of its two radial slots and its two weights per edge.
 // The perm entries of a batch are fetched two batches ahead and every load is
-// unconditional (absent edges read a valid substitute), so each data load is
-// issued one batch before it is consumed and no load waits on another.
-// Accumulation order and arithmetic are the same as in zs_fwd_kernel.
+// unconditional (absent edges and channels read a valid substitute), so each
+// data load is issued one batch before it is consumed and no load waits on
+// another.  Accumulation order and arithmetic are those of zs_fwd_kernel.
 // ---------------------------------------------------------------------------
-#ifndef ZS_FWD_BATCH
-#define ZS_FWD_BATCH 8
-#endif
-constexpr int kFwdBatch = ZS_FWD_BATCH;
-constexpr int kFwdRadVec = kFwdBatch * kSlots * 8 / 64;   // float4 per lane per batch (6)
-constexpr int kFwdCplVec = (kFwdBatch * kZonal + 63) / 64; // floats per lane per batch (4)
-
-struct FwdRegs {
-    float4 r[kFwdRadVec];
-    float w[kFwdCplVec];
+template <int VEC, int B>
+struct FwdShape {
+    static constexpr int T = 8 * VEC;                   // channels per tile
+    static constexpr int F4 = T / 4;                    // float4 per slot row of a tile
+    static constexpr int RAD = B * kSlots * F4;         // radial float4 per batch
+    static constexpr int RV = (RAD + 63) / 64;          // radial float4 per lane
+    static constexpr int CV = (B * (kZonal + 1) + 63) / 64;   // coupling/env floats per lane
 };
 
-// Lane mapping of the coalesced batch fetch (i = fetch slot, lane = 0..63):
-//   radial float4 f = i*64 + lane -> batch edge f / 24, slot (f % 24) / 8, quad f % 8
-//   coupling float idx = i*64 + lane -> batch edge idx / 15, column idx % 15 (idx < 240)
-__device__ __attribute__((always_inline)) inline int fwd_rad_edge(int i, int lane) {
-    return (i * 64 + lane) / (kSlots * 8);
-}
-__device__ __attribute__((always_inline)) inline int fwd_rad_rem(int i, int lane) {
-    return (i * 64 + lane) % (kSlots * 8);
-}
-__device__ __attribute__((always_inline)) inline int fwd_cpl_idx(int i, int lane) {
-    return i * 64 + lane;
-}
+template <int VEC, int B>
+struct FwdRegs {
+    float4 r[FwdShape<VEC, B>::RV];
+    float w[FwdShape<VEC, B>::CV];
+};
 
 // A batch's perm entries, fetched one batch before they are used.  Every lane
 // issues its load from a valid position (clamped to the node's last edge) and
@@ -199,75 +192,128 @@ __device__ __attribute__((always_inline)) inline int perm_resolve(PermRaw p, int
     return (p.valid && p.raw >= 0 && p.raw < n_edges) ? p.raw : -1;
 }
 
-// Loads of one batch, all unconditional: absent edges and channels past C read
-// a valid substitute (edge 0, the tile's first channel) that is never used.
-// With NORM, the fetch slots after the batch's 15 * kFwdBatch coupling floats
-// carry the edges' envelope factors (one per edge).
-template <bool NORM>
-__device__ __attribute__((always_inline)) inline void fwd_fetch(FwdRegs& R, int lane, int pe,
-                                                                 const float* __restrict__ coupling,
-                                                                 const float* __restrict__ radial,
-                                                                 const float* __restrict__ env,
-                                                                 const InLayout& L, int64_t C,
-                                                                 int64_t cbase) {
+// Loads of one batch, all unconditional: absent edges, channels past C and
+// fetch slots past the batch read a valid substitute (edge 0, the tile's
+// first channel) that is never used.  Radial float4 f = i*64 + lane is batch
+// edge f / (3*F4), slot (f % (3*F4)) / F4, float4 f % F4 of the tile; coupling
+// float idx = i*64 + lane is batch edge idx / 15, column idx % 15 for
+// idx < 15*B, and with NORM the envelope factor of batch edge idx - 15*B for
+// the next B slots.
+template <int VEC, int B, bool NORM>
+__device__ __attribute__((always_inline)) inline void fwd_fetch(
+    FwdRegs<VEC, B>& R, int lane, int pe, const float* __restrict__ coupling,
+    const float* __restrict__ radial, const float* __restrict__ env, const InLayout& L, int64_t C,
+    int64_t cbase) {
+    using S = FwdShape<VEC, B>;
 #pragma unroll
-    for (int i = 0; i < kFwdRadVec; ++i) {
-        const int rem = fwd_rad_rem(i, lane);
-        const int64_t ch = cbase + (rem & 7) * 4;
-        const int e = __shfl(pe, fwd_rad_edge(i, lane), 64);
+    for (int i = 0; i < S::RV; ++i) {
+        const int f = i * 64 + lane;
+        const int rem = f % (kSlots * S::F4);
+        const int64_t ch = cbase + (rem % S::F4) * 4;
+        const int e = __shfl(pe, f < S::RAD ? f / (kSlots * S::F4) : 0, 64);
         const int64_t es = e >= 0 ? e : 0;
         const int64_t cs = ch < C ? ch : cbase;
-        R.r[i] = load_stream4<ZS_FWD_NT != 0>(radial + es * L.rad_edge + (rem >> 3) * L.rad_slot +
-                                              cs);
+        R.r[i] = load_stream4<ZS_FWD_NT != 0>(radial + es * L.rad_edge +
+                                              (rem / S::F4) * L.rad_slot + cs);
     }
 #pragma unroll
-    for (int i = 0; i < kFwdCplVec; ++i) {
-        const int idx = fwd_cpl_idx(i, lane);
-        const bool in = idx < kFwdBatch * kZonal;
-        const bool in_env = NORM && !in && idx < kFwdBatch * (kZonal + 1);
-        const int b = in ? idx / kZonal : (in_env ? idx - kFwdBatch * kZonal : 0);
+    for (int i = 0; i < S::CV; ++i) {
+        const int idx = i * 64 + lane;
+        const bool in = idx < B * kZonal;
+        const bool in_env = NORM && !in && idx < B * (kZonal + 1);
+        const int b = in ? idx / kZonal : (in_env ? idx - B * kZonal : 0);
         const int e = __shfl(pe, b, 64);
         const int64_t es = e >= 0 ? e : 0;
         R.w[i] = in_env ? env[es] : coupling[es * L.cpl_edge + (in ? idx % kZonal : 0)];
     }
 }
 
+// VEC consecutive floats from LDS with the widest accesses their alignment
+// allows (q*VEC floats into a 32-byte aligned row).
+template <int VEC>
+__device__ __attribute__((always_inline)) inline void lds_read(const float* p, float (&v)[VEC]) {
+    if constexpr (VEC % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i) {
+            const float4 t = reinterpret_cast<const float4*>(p)[i];
+            v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+        }
+    } else if constexpr (VEC % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i) {
+            const float2 t = reinterpret_cast<const float2*>(p)[i];
+            v[2 * i] = t.x; v[2 * i + 1] = t.y;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) v[i] = p[i];
+    }
+}
+
+// Stores VEC consecutive floats of an output row; n_valid < VEC masks the
+// channels past C.  Rows are 16-byte aligned (C % 4 == 0).
+template <int VEC>
+__device__ __attribute__((always_inline)) inline void row_store(float* p, const float (&v)[VEC],
+                                                                int n_valid) {
+    if (n_valid >= VEC) {
+        if constexpr (VEC % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < VEC / 4; ++i)
+                reinterpret_cast<float4*>(p)[i] =
+                    make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+        } else if constexpr (VEC % 2 == 0) {
+#pragma unroll
+            for (int i = 0; i < VEC / 2; ++i)
+                reinterpret_cast<float2*>(p)[i] = make_float2(v[2 * i], v[2 * i + 1]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) p[i] = v[i];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+            if (i < n_valid) p[i] = v[i];
+    }
+}
+
 // With NORM the envelope factor of batch edge b sits in csh[b * 16 + 15] and
 // deg accumulates the envelopes in edge order (fp32 adds from +0).
-template <bool NORM>
+template <int VEC, int B, bool NORM>
 __device__ __attribute__((always_inline)) inline void fwd_stage_accumulate(
-    const FwdRegs& R, float4* rsh, float* csh, int cnt, int lane, int q, int j, int sA, int sB,
-    float (&acc0)[4], float (&acc1)[4], float& deg) {
+    const FwdRegs<VEC, B>& R, float4* rsh, float* csh, int cnt, int lane, int q, int j, int sA,
+    int sB, float (&acc0)[VEC], float (&acc1)[VEC], float& deg) {
+    using S = FwdShape<VEC, B>;
 #pragma unroll
-    for (int i = 0; i < kFwdRadVec; ++i) rsh[i * 64 + lane] = R.r[i];
+    for (int i = 0; i < S::RV; ++i)
+        if (S::RAD % 64 == 0 || i * 64 + lane < S::RAD) rsh[i * 64 + lane] = R.r[i];
 #pragma unroll
-    for (int i = 0; i < kFwdCplVec; ++i) {
-        const int idx = fwd_cpl_idx(i, lane);
-        if (idx < kFwdBatch * kZonal)
+    for (int i = 0; i < S::CV; ++i) {
+        const int idx = i * 64 + lane;
+        if (idx < B * kZonal)
             csh[(idx / kZonal) * 16 + idx % kZonal] = R.w[i];
-        else if (NORM && idx < kFwdBatch * (kZonal + 1))
-            csh[(idx - kFwdBatch * kZonal) * 16 + 15] = R.w[i];
+        else if (NORM && idx < B * (kZonal + 1))
+            csh[(idx - B * kZonal) * 16 + 15] = R.w[i];
     }
+    const float* rf = reinterpret_cast<const float*>(rsh);
     auto edge = [&](int b) {
         if (NORM) deg = deg + csh[b * 16 + 15];
-        const float4 xa = rsh[b * (kSlots * 8) + sA * 8 + q];
-        const float4 xb = rsh[b * (kSlots * 8) + sB * 8 + q];
+        float xa[VEC], xb[VEC];
+        lds_read<VEC>(rf + (b * kSlots + sA) * S::T + q * VEC, xa);
+        lds_read<VEC>(rf + (b * kSlots + sB) * S::T + q * VEC, xb);
         const float w0 = csh[b * 16 + 2 * j];
         const float w1 = csh[b * 16 + 2 * j + 1];
-        float m;
-        m = w0 * xa.x; acc0[0] = acc0[0] + m;
-        m = w0 * xa.y; acc0[1] = acc0[1] + m;
-        m = w0 * xa.z; acc0[2] = acc0[2] + m;
-        m = w0 * xa.w; acc0[3] = acc0[3] + m;
-        m = w1 * xb.x; acc1[0] = acc1[0] + m;
-        m = w1 * xb.y; acc1[1] = acc1[1] + m;
-        m = w1 * xb.z; acc1[2] = acc1[2] + m;
-        m = w1 * xb.w; acc1[3] = acc1[3] + m;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            float m = w0 * xa[v];
+            acc0[v] = acc0[v] + m;
+            m = w1 * xb[v];
+            acc1[v] = acc1[v] + m;
+        }
     };
-    if (cnt == kFwdBatch) {
+    if (cnt == B) {
         // full batch: unrolled so the LDS reads of all its edges are in flight
 #pragma unroll
-        for (int b = 0; b < kFwdBatch; ++b) edge(b);
+        for (int b = 0; b < B; ++b) edge(b);
     } else {
         for (int b = 0; b < cnt; ++b) edge(b);
     }
@@ -276,7 +322,7 @@ __device__ __attribute__((always_inline)) inline void fwd_stage_accumulate(
 // NORM: also accumulate each node's envelope sum deg in edge order and write
 // y = out * norm with norm = 1/sqrt(deg) (0 for deg <= 0); out (the
 // unnormalised sum) is written only when the pointer is non-null.
-template <bool NORM>
+template <int VEC, int B, bool NORM>
 __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restrict__ coupling,
                                                            const float* __restrict__ radial,
                                                            InLayout L,
@@ -285,9 +331,11 @@ __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restri
                                                            int64_t n_nodes, int64_t n_edges,
                                                            int64_t C, float* __restrict__ out,
                                                            NormIO nio) {
-    static_assert(kFwdCplVec * 64 >= kFwdBatch * (kZonal + 1), "envelope slots");
-    __shared__ float4 rsh[kFwdBatch * kSlots * 8];
-    __shared__ float csh[kFwdBatch * 16];
+    using S = FwdShape<VEC, B>;
+    static_assert(S::CV * 64 >= B * (kZonal + 1), "coupling and envelope slots");
+    static_assert(B <= 64, "one perm entry per lane");
+    __shared__ float4 rsh[S::RAD];
+    __shared__ float csh[B * 16];
 
     const int lane = threadIdx.x;
     const int q = lane & 7;
@@ -295,74 +343,98 @@ __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restri
     const int rA = 2 * j + 1;                 // rows rA, rA + 1 (rA + 1 == 16 is row 0)
     const int sA = row_slot(rA);
     const int sB = row_slot(rA + 1 <= kZonal ? rA + 1 : kZonal);
-    const int64_t cbase = int64_t(blockIdx.y) * 32;
-    const int64_t c0 = cbase + q * 4;
-    const bool act = c0 < C;
+    const int64_t cbase = int64_t(blockIdx.y) * S::T;
+    const int64_t c0 = cbase + q * VEC;
+    const int n_valid = c0 >= C ? 0 : (C - c0 < VEC ? int(C - c0) : VEC);
 
-    if (lane < kFwdBatch) csh[lane * 16 + 15] = 0.0f;   // pad column, never fetched
+    if (lane < B) csh[lane * 16 + 15] = 0.0f;   // pad column, never fetched
 
     for (int64_t node = blockIdx.x; node < n_nodes; node += gridDim.x) {
         int64_t k0 = rowptr[node];
         int64_t k1 = rowptr[node + 1];
         k0 = k0 < 0 ? 0 : (k0 > n_edges ? n_edges : k0);
         k1 = k1 < k0 ? k0 : (k1 > n_edges ? n_edges : k1);
-        const int64_t nb = (k1 - k0 + kFwdBatch - 1) / kFwdBatch;
+        const int64_t nb = (k1 - k0 + B - 1) / B;
 
-        float acc0[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        float acc1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float acc0[VEC], acc1[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc0[v] = acc1[v] = 0.0f;
         float deg = 0.0f;
         auto batch_count = [k0, k1](int64_t t) {
-            const int64_t kb = k0 + t * kFwdBatch;
-            return int(k1 - kb < kFwdBatch ? k1 - kb : kFwdBatch);
+            const int64_t kb = k0 + t * B;
+            return int(k1 - kb < B ? k1 - kb : B);
         };
 
         if (nb > 0) {
-            FwdRegs RA, RB;
-            PermRaw rA = perm_issue(perm, k0, k1, lane, kFwdBatch);
-            PermRaw rB = perm_issue(perm, k0 + kFwdBatch, k1, lane, kFwdBatch);
-            fwd_fetch<NORM>(RA, lane, perm_resolve(rA, n_edges), coupling, radial, nio.env, L, C,
-                            cbase);
+            FwdRegs<VEC, B> RA, RB;
+            PermRaw pA = perm_issue(perm, k0, k1, lane, B);
+            PermRaw pB = perm_issue(perm, k0 + B, k1, lane, B);
+            fwd_fetch<VEC, B, NORM>(RA, lane, perm_resolve(pA, n_edges), coupling, radial,
+                                    nio.env, L, C, cbase);
             for (int64_t t = 0; t < nb; t += 2) {
-                const PermRaw rN = perm_issue(perm, k0 + (t + 2) * kFwdBatch, k1, lane, kFwdBatch);
-                fwd_fetch<NORM>(RB, lane, perm_resolve(rB, n_edges), coupling, radial, nio.env, L,
-                                C, cbase);
-                fwd_stage_accumulate<NORM>(RA, rsh, csh, batch_count(t), lane, q, j, sA, sB, acc0,
-                                           acc1, deg);
+                const PermRaw pN = perm_issue(perm, k0 + (t + 2) * B, k1, lane, B);
+                fwd_fetch<VEC, B, NORM>(RB, lane, perm_resolve(pB, n_edges), coupling, radial,
+                                        nio.env, L, C, cbase);
+                fwd_stage_accumulate<VEC, B, NORM>(RA, rsh, csh, batch_count(t), lane, q, j, sA,
+                                                   sB, acc0, acc1, deg);
                 if (t + 1 >= nb) break;
-                rB = perm_issue(perm, k0 + (t + 3) * kFwdBatch, k1, lane, kFwdBatch);
-                fwd_fetch<NORM>(RA, lane, perm_resolve(rN, n_edges), coupling, radial, nio.env, L,
-                                C, cbase);
-                fwd_stage_accumulate<NORM>(RB, rsh, csh, batch_count(t + 1), lane, q, j, sA, sB,
-                                           acc0, acc1, deg);
+                pB = perm_issue(perm, k0 + (t + 3) * B, k1, lane, B);
+                fwd_fetch<VEC, B, NORM>(RA, lane, perm_resolve(pN, n_edges), coupling, radial,
+                                        nio.env, L, C, cbase);
+                fwd_stage_accumulate<VEC, B, NORM>(RB, rsh, csh, batch_count(t + 1), lane, q, j,
+                                                   sA, sB, acc0, acc1, deg);
             }
         }
 
+        float zero[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) zero[v] = 0.0f;
         if (NORM) {
             const float nrm = deg > 0.0f ? 1.0f / sqrtf(deg) : 0.0f;
             if (lane == 0 && blockIdx.y == 0) nio.norm[node] = nrm;
-            if (act) {
-                float* ynode = nio.y + node * kRows * C + c0;
-                float4 v0, v1;
-                v0.x = acc0[0] * nrm; v0.y = acc0[1] * nrm; v0.z = acc0[2] * nrm; v0.w = acc0[3] * nrm;
-                v1.x = acc1[0] * nrm; v1.y = acc1[1] * nrm; v1.z = acc1[2] * nrm; v1.w = acc1[3] * nrm;
-                *reinterpret_cast<float4*>(ynode + int64_t(rA) * C) = v0;
-                if (rA + 1 <= kZonal)
-                    *reinterpret_cast<float4*>(ynode + int64_t(rA + 1) * C) = v1;
-                else
-                    *reinterpret_cast<float4*>(ynode) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            float y0[VEC], y1[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                y0[v] = acc0[v] * nrm;
+                y1[v] = acc1[v] * nrm;
             }
-        }
-        if (act && (!NORM || out != nullptr)) {
-            float* onode = out + node * kRows * C + c0;
-            *reinterpret_cast<float4*>(onode + int64_t(rA) * C) =
-                make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
+            float* ynode = nio.y + node * kRows * C + c0;
+            row_store<VEC>(ynode + int64_t(rA) * C, y0, n_valid);
             if (rA + 1 <= kZonal)
-                *reinterpret_cast<float4*>(onode + int64_t(rA + 1) * C) =
-                    make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
+                row_store<VEC>(ynode + int64_t(rA + 1) * C, y1, n_valid);
             else
-                *reinterpret_cast<float4*>(onode) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                row_store<VEC>(ynode, zero, n_valid);
+        }
+        if (!NORM || out != nullptr) {
+            float* onode = out + node * kRows * C + c0;
+            row_store<VEC>(onode + int64_t(rA) * C, acc0, n_valid);
+            if (rA + 1 <= kZonal)
+                row_store<VEC>(onode + int64_t(rA + 1) * C, acc1, n_valid);
+            else
+                row_store<VEC>(onode, zero, n_valid);
         }
     }
+}
+
+template <int VEC, int B>
+void launch_staged(const float* coupling, const float* radial, InLayout L, const int32_t* rowptr,
+                   const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels,
+                   float* out, NormIO nio, unsigned gx, hipStream_t stream) {
+    const unsigned gy = unsigned((channels + 8 * VEC - 1) / (8 * VEC));
+    if (nio.y != nullptr)   // env may be NULL when there are no edges
+        zs_fwd_staged_kernel<VEC, B, true><<<dim3(gx, gy), 64, 0, stream>>>(
+            coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
+    else
+        zs_fwd_staged_kernel<VEC, B, false><<<dim3(gx, gy), 64, 0, stream>>>(
+            coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
+}
+
+// Channel tiling of the staged forward: one tile of VEC = ceil(C / 8)
+// channels per lane up to 64 channels; beyond that, tiles of 64 channels, so
+// every tile starts on a 256-byte boundary of a radial row (narrower tiles
+// would split 128-byte lines between two wavefronts).
+int forward_tile_vec(int64_t channels) {
+    return channels > 64 ? 8 : int((channels + 7) / 8);
 }
 
 }  // namespace
@@ -373,19 +445,25 @@ hipError_t launch_forward(const float* coupling, const float* radial, InLayout L
                           NormIO nio, hipStream_t stream) {
     constexpr int64_t kGridCap = 1 << 20;
     const unsigned gx = unsigned(n_nodes < kGridCap ? n_nodes : kGridCap);
-    const bool norm = nio.y != nullptr;   // env may be NULL when there are no edges
     if (vec4) {
-        const unsigned gy = unsigned((channels + 31) / 32);
-        if (norm)
-            zs_fwd_staged_kernel<true><<<dim3(gx, gy), 64, 0, stream>>>(
-                coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
-        else
-            zs_fwd_staged_kernel<false><<<dim3(gx, gy), 64, 0, stream>>>(
-                coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
+#define ZS_FWD_STAGED(V, BB)                                                                     \
+    launch_staged<V, BB>(coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio, \
+                         gx, stream)
+        switch (forward_tile_vec(channels)) {
+            case 1: ZS_FWD_STAGED(1, 8); break;
+            case 2: ZS_FWD_STAGED(2, 8); break;
+            case 3: ZS_FWD_STAGED(3, 8); break;
+            case 4: ZS_FWD_STAGED(4, 8); break;
+            case 5: ZS_FWD_STAGED(5, 4); break;
+            case 6: ZS_FWD_STAGED(6, 4); break;
+            case 7: ZS_FWD_STAGED(7, 4); break;
+            default: ZS_FWD_STAGED(8, 4); break;
+        }
+#undef ZS_FWD_STAGED
     } else {
         constexpr int NQ = 16, VEC = 1;
         const unsigned gy = unsigned((channels + NQ * VEC - 1) / (NQ * VEC));
-        if (norm)
+        if (nio.y != nullptr)
             zs_fwd_kernel<VEC, NQ, 8, true><<<dim3(gx, gy), 64, 0, stream>>>(
                 coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
         else

@@ -106,6 +106,11 @@ def test_normalized_workloads(dev, name):
 NORM_CASES = [
     # (label, N, E, C, dst kind) -- channel counts that take each kernel variant
     ("c4", 9, 300, 4, "uniform"),
+    ("c8", 9, 300, 8, "uniform"),
+    ("c24", 9, 300, 24, "uniform"),
+    ("c48", 9, 300, 48, "uniform"),
+    ("c56", 9, 300, 56, "uniform"),
+    ("c100", 9, 300, 100, "uniform"),
     ("c20_scalar", 11, 500, 20, "uniform"),
     ("c36", 13, 700, 36, "uniform"),
     ("c64", 17, 900, 64, "uniform"),

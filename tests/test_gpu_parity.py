@@ -144,14 +144,26 @@ EDGE_CASES = [
     ("c2", 17, 500, 2, "uniform"),
     ("c3", 17, 500, 3, "uniform"),
     ("c5", 17, 500, 5, "uniform"),
+    ("c4", 17, 500, 4, "uniform"),
+    ("c12", 17, 500, 12, "uniform"),
+    ("c16", 17, 500, 16, "uniform"),
+    ("c24", 17, 500, 24, "uniform"),
+    ("c28", 17, 500, 28, "uniform"),
     ("c31", 17, 500, 31, "uniform"),
     ("c33", 17, 500, 33, "uniform"),
     ("c36", 17, 500, 36, "uniform"),
     ("c40_pages", 33, 777, 40, "uniform"),
+    ("c44", 17, 500, 44, "uniform"),
+    ("c48", 17, 500, 48, "uniform"),
+    ("c52", 17, 500, 52, "uniform"),
+    ("c56", 17, 500, 56, "uniform"),
+    ("c60", 17, 500, 60, "uniform"),
     ("c63", 17, 500, 63, "uniform"),
     ("c64", 17, 500, 64, "uniform"),
     ("c65", 17, 500, 65, "uniform"),
+    ("c68", 17, 500, 68, "uniform"),
     ("c96", 17, 500, 96, "uniform"),
+    ("c100", 17, 500, 100, "uniform"),
     ("c128", 17, 700, 128, "uniform"),
     ("c260", 9, 300, 260, "uniform"),
     ("c1024", 3, 70, 1024, "uniform"),
