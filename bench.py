@@ -224,6 +224,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline", choices=sorted(synthetic.WORKLOADS))
+    ap.add_argument("--channels", type=int, default=None,
+                    help="run the workload's frame (same N, E, destinations and seed) with this "
+                         "channel count instead of its own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--inputs", default="contiguous", choices=["contiguous", "views"],
                     help="views: coupling read in place from a packed (E, 46) Wigner band and "
@@ -248,6 +251,9 @@ def main() -> int:
     import edge_node_scatter_amd as zs
 
     w = synthetic.WORKLOADS[args.workload]
+    if args.channels is not None and args.channels != w.channels:
+        w = synthetic.custom(f"{w.name}_c{args.channels}", w.n_nodes, w.n_edges, args.channels,
+                             w.seed, w.dst_kind, w.envelope)
     x = synthetic.make_inputs(w)
     dev = torch.device("cuda:0")
     zs.load()
@@ -311,7 +317,9 @@ def main() -> int:
     fb_us = fwd_us + bwd_us
     gbs = (nb["fwd"] + nb["bwd"]) / (fb_us * 1e-6) / 1e9
     bwd_gbs = nb["bwd"] / (bwd_us * 1e-6) / 1e9
-    traffic = load_traffic("zs_bwd_staged_kernel")
+    # the committed counter summary covers the headline frame with contiguous inputs only
+    traffic = (load_traffic("zs_bwd_staged_kernel")
+               if w.name == "headline" and args.inputs == "contiguous" else None)
 
     rec = {
         "metric": METRIC,
