@@ -189,6 +189,29 @@ def cpu_baseline(x, w, budget_s: float = 12.0) -> dict:
     }
 
 
+def time_flushed(zs, torch, cpl, rad, g, csr, out, gc, gr, dev, nb, steps: int) -> dict:
+    """Forward + backward with the caches flushed first: a 512 MiB buffer is
+    overwritten before every sample (larger than the 256 MB memory-side cache
+    and the L2s), then forward and backward run between two events."""
+    scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    ms = []
+    for i in range(steps + 2):
+        scratch.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        zs.zs_forward(cpl, rad, csr, out=out)
+        zs.zs_backward(g, cpl, rad, csr, grad_coupling=gc, grad_radial=gr)
+        b.record()
+        ms.append((a, b))
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) * 1e3 for a, b in ms[2:]]
+    med = statistics.median(t)
+    gbs = (nb["fwd"] + nb["bwd"]) / (med * 1e-6) / 1e9
+    return {"fwd_bwd_us_median": round(med, 2), "gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "samples": len(t),
+            "note": "512 MiB buffer overwritten before each sample"}
+
+
 def time_normalized(zs, torch, cpl, rad, x, csr, dev, steps: int) -> dict:
     """The same frame through the fused degree normalisation
     (zs_forward_normalized + zs_backward_normalized, CSR reused), timed with
@@ -360,6 +383,8 @@ def main() -> int:
         },
         "source_hash": {fam: kernel_source_hash(fam) for fam in KERNEL_SOURCES},
     }
+    rec["flushed"] = time_flushed(zs, torch, cpl, rad, g, csr, out, gc, gr, dev, nb,
+                                  min(args.steps, 20))
     rec["normalized"] = time_normalized(zs, torch, cpl, rad, x, csr, dev, args.steps)
     if args.calibrate_copy:
         src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)

@@ -220,6 +220,29 @@ def test_bad_destination_rejected(dev):
         assert ei.value.status == -3
 
 
+CSR_ONLY_CASES = [
+    # (label, N, E): node counts around the bucket-size limits of the CSR build
+    ("n_4194304_lds_nodes", 1 << 22, 100000),        # 2048-node buckets, LDS tables
+    ("n_4194305_global_nodes", (1 << 22) + 1, 100000),  # 4096-node buckets, global tables
+    ("n_5000000_sparse", 5_000_000, 30000),
+    ("n_65536_many_buckets", 1 << 16, 700000),
+    ("n_1_all_one_node", 1, 100000),
+]
+
+
+@pytest.mark.parametrize("label,N,E", CSR_ONLY_CASES, ids=[c[0] for c in CSR_ONLY_CASES])
+def test_csr_only_node_counts(dev, label, N, E):
+    say(f"[gpu] csr {label}: N={N} E={E}")
+    rng = np.random.default_rng(N % 1000 + E)
+    dst = rng.integers(0, N, E, dtype=np.int64)
+    csr = zs.zs_build_csr(torch.from_numpy(dst).to(dev), N)
+    torch.cuda.synchronize()
+    rowptr, perm = oracle.csr(dst, N)
+    assert np.array_equal(csr.rowptr.cpu().numpy(), rowptr), f"{label}: rowptr"
+    assert np.array_equal(csr.perm.cpu().numpy(), perm), f"{label}: perm"
+    assert np.array_equal(csr.dst32.cpu().numpy(), dst.astype(np.int32)), f"{label}: dst32"
+
+
 def test_guard_regions_and_unaligned(dev):
     """Outputs inside NaN-poisoned buffers: nothing outside them is written and
     nothing past the inputs is read; a one-float offset takes the scalar path."""
