@@ -43,7 +43,7 @@ _CSRC = os.path.join(ROOT, "edge_node_scatter_amd", "csrc")
 KERNEL_SOURCES = {
     "fwd": ["zs_fwd.hip", "zs_internal.h"],
     "bwd": ["zs_bwd.hip", "zs_internal.h"],
-    "csr": ["zs_csr.hip", "zs_internal.h"],
+    "csr": ["zs_csr.hip", "zs_csr.h", "zs_internal.h"],
     "norm": ["zs_norm.hip", "zs_internal.h"],
 }
 

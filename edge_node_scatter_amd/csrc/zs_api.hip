@@ -3,6 +3,7 @@
 // call leaves device state untouched.
 #include "zs.h"
 
+#include "zs_csr.h"
 #include "zs_internal.h"
 
 namespace {

@@ -33,7 +33,7 @@
 //
 // Every destination is range-checked; an out-of-range one is never used as an
 // index and raises the validation flag.
-#include "zs_internal.h"
+#include "zs_csr.h"
 
 namespace zs {
 

@@ -69,30 +69,6 @@ __device__ __attribute__((always_inline)) inline void store_stream4(float* p, fl
 #define ZS_BWD_NT 1
 #endif
 
-// ---- CSR build ------------------------------------------------------------
-struct CsrPlan {
-    int64_t tiles;        // edge tiles of the bucket level
-    int64_t tile_edges;   // edges per tile (last tile may be shorter)
-    int bucket_shift;     // SB: a bucket holds 2^SB consecutive nodes
-    int bucket_bits;      // ceil(log2(buckets))
-    int64_t buckets;      // NB
-    bool node_lds;        // per-bucket node tables fit in LDS
-    size_t off_flag;      // int32 error flag
-    size_t off_tile_bad;  // int32 [tiles] per-tile out-of-range indicator
-    size_t off_counts;    // int32 [tiles][buckets] per-tile counts, then offsets
-    size_t off_tot;       // int32 [buckets] bucket totals
-    size_t off_starts;    // int32 [buckets + 1] bucket starts
-    size_t off_pairs;     // int2 [n_edges] (destination, edge) grouped by bucket
-    size_t off_scratch;   // int32 [n_nodes] node offsets (only without node_lds)
-    size_t bytes;         // total workspace bytes
-};
-CsrPlan plan_csr(int64_t n_edges, int64_t n_nodes);
-// flag: device int32 that receives the out-of-range indicator; NULL selects
-// the one inside the workspace (at plan.off_flag).
-hipError_t launch_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* rowptr,
-                      int32_t* perm, int32_t* dst32, void* workspace, const CsrPlan& plan,
-                      int32_t* flag, hipStream_t stream);
-
 // ---- forward / backward -----------------------------------------------------
 // Strides (in floats) of the two edge inputs.  Coupling columns and radial
 // channels are unit-stride; a contiguous layout is {15, 3*C, C}.
