@@ -161,7 +161,8 @@ int backward_impl(const float* grad_out, const float* coupling, int64_t cs, cons
                       aligned(grad_radial, 16) && re % 4 == 0 && rs % 4 == 0;
     return hip_status(zs::launch_backward(grad_out, coupling, radial, zs::InLayout{cs, re, rs},
                                           dst32, rowptr, perm, n_nodes, n_edges, channels,
-                                          grad_coupling, grad_radial, vec4, nullptr, s));
+                                          grad_coupling, grad_radial, vec4,
+                                          zs::NormGrad{nullptr, nullptr, nullptr}, nullptr, s));
 }
 
 }  // namespace
@@ -267,17 +268,21 @@ int zs_backward_normalized(const float* grad_y, const float* out, const float* n
             if (overlap(outs[i], in)) return ZS_ERR_ALIAS;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    bool deg_done = false;
     if (n_edges > 0) {
         const bool vec4 = channels % 4 == 0 && aligned(grad_y, 16) && aligned(radial, 16) &&
                           aligned(grad_radial, 16);
+        // the degree gradient is formed inside the backward when out can be
+        // read in 16-byte pieces beside grad_y
+        const bool fuse = aligned(out, 16);
         const hipError_t err = zs::launch_backward(
             grad_y, coupling, radial, zs::InLayout{zs::kZonal, zs::kSlots * channels, channels},
             dst32, rowptr, perm, n_nodes, n_edges, channels, grad_coupling, grad_radial, vec4,
-            norm, s);
+            zs::NormGrad{norm, fuse ? out : nullptr, fuse ? grad_deg : nullptr}, &deg_done, s);
         if (err != hipSuccess) return ZS_ERR_HIP;
     }
     return hip_status(zs::launch_norm_grad(grad_y, out, norm, dst32, n_nodes, n_edges, channels,
-                                           grad_deg, grad_env, s));
+                                           grad_deg, grad_env, deg_done, s));
 }
 
 }  // extern "C"

@@ -482,8 +482,7 @@ void zs_bwd_staged_kernel(
     const float* __restrict__ grad_out, const float* __restrict__ coupling,
     const float* __restrict__ radial, InLayout L, const int32_t* __restrict__ rowptr,
     const int32_t* __restrict__ perm, int64_t n_nodes, int64_t n_edges, int64_t C,
-    float* __restrict__ grad_coupling, float* __restrict__ grad_radial,
-    const float* __restrict__ norm) {
+    float* __restrict__ grad_coupling, float* __restrict__ grad_radial, NormGrad ng) {
     constexpr int EPW = 64 / NQ;
     constexpr int T = NQ * VEC;
     static_assert(T % 4 == 0, "the upstream rows are staged as float4");
@@ -503,18 +502,37 @@ void zs_bwd_staged_kernel(
         int64_t k1 = rowptr[node + 1];
         k0 = k0 < 0 ? 0 : (k0 > n_edges ? n_edges : k0);
         k1 = k1 < k0 ? k0 : (k1 > n_edges ? n_edges : k1);
-        if (k0 >= k1) continue;
+        const bool deg = ng.grad_deg != nullptr;   // also form the degree gradient
+        if (k0 >= k1 && !deg) continue;
         const float* gnode = grad_out + node * kRows * C;
-        const float gs = norm != nullptr ? norm[node] : 1.0f;   // see zs_bwd_kernel
+        const float gs = ng.norm != nullptr ? ng.norm[node] : 1.0f;   // see zs_bwd_kernel
+        double s = 0.0;   // degree gradient: sum of grad_out * out over rows 1..15
         for (int i = lane; i < kZonal * T / 4; i += 64) {
             const int r = i / (T / 4) + 1;
             const int64_t c = int64_t(i % (T / 4)) * 4;
             float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             if (c < C) {
                 v = *reinterpret_cast<const float4*>(gnode + int64_t(r) * C + c);
+                if (deg) {
+                    const float4 o = *reinterpret_cast<const float4*>(
+                        ng.out + (node * kRows + r) * C + c);
+                    s = __builtin_fma(double(v.x), double(o.x), s);
+                    s = __builtin_fma(double(v.y), double(o.y), s);
+                    s = __builtin_fma(double(v.z), double(o.z), s);
+                    s = __builtin_fma(double(v.w), double(o.w), s);
+                }
                 v.x = v.x * gs; v.y = v.y * gs; v.z = v.z * gs; v.w = v.w * gs;
             }
             gsh4[i] = v;
+        }
+        if (deg) {
+#pragma unroll
+            for (int h = 32; h >= 1; h >>= 1) s = s + __shfl_xor(s, h, 64);
+            if (lane == 0) {
+                const double t = ng.norm[node];
+                ng.grad_deg[node] = t == 0.0 ? 0.0f : float(-0.5 * t * t * t * s);
+            }
+            if (k0 >= k1) continue;
         }
         const int64_t nsteps = (k1 - k0 + EPW - 1) / EPW;
         BwdRegs<NQ, VEC> A, B;
@@ -567,7 +585,9 @@ hipError_t launch_backward(const float* grad_out, const float* coupling, const f
                            InLayout L, const int32_t* dst32, const int32_t* rowptr,
                            const int32_t* perm, int64_t n_nodes, int64_t n_edges,
                            int64_t channels, float* grad_coupling, float* grad_radial, bool vec4,
-                           const float* norm, hipStream_t stream) {
+                           NormGrad ng, bool* deg_done, hipStream_t stream) {
+    const float* norm = ng.norm;
+    if (deg_done) *deg_done = false;
     (void)dst32;   // this traversal is CSR-major; dst32 serves edge-major variants
     constexpr int64_t kGridCap = 1 << 20;
     const unsigned gx = unsigned(n_nodes < kGridCap ? n_nodes : kGridCap);
@@ -580,11 +600,12 @@ hipError_t launch_backward(const float* grad_out, const float* coupling, const f
         if (channels == (NQ) * (VEC))                                                            \
             zs_bwd_staged_kernel<NQ, VEC, true><<<gx, 64, 0, stream>>>(                          \
                 grad_out, coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels,         \
-                grad_coupling, grad_radial, norm);                                               \
+                grad_coupling, grad_radial, ng);                                                 \
         else                                                                                     \
             zs_bwd_staged_kernel<NQ, VEC, false><<<gx, 64, 0, stream>>>(                         \
                 grad_out, coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels,         \
-                grad_coupling, grad_radial, norm);                                               \
+                grad_coupling, grad_radial, ng);                                                 \
+        if (deg_done) *deg_done = ng.grad_deg != nullptr;                                        \
     } while (0)
     int nq = 0, vec = 0;
     if (vec4 && backward_layout(channels, nq, vec)) {

@@ -94,19 +94,30 @@ hipError_t launch_forward(const float* coupling, const float* radial, InLayout L
                           int64_t n_edges, int64_t channels, float* out, bool vec4,
                           NormIO nio, hipStream_t stream);
 
-// norm: null for the plain backward; else grad_out is the gradient of y and is
-// multiplied by norm[dst] (fp32) on load.
+// Normalised backward.  norm == nullptr: plain backward.  Otherwise grad_out is
+// the gradient of y and is multiplied by norm[dst] (fp32) on load, and when
+// out and grad_deg are non-null the staged kernel also forms the degree
+// gradient grad_deg[n] = -1/2 t^3 sum_{r>=1,c} grad_out * out (t = norm[n])
+// while it stages the node's rows.
+struct NormGrad {
+    const float* norm;
+    const float* out;
+    float* grad_deg;
+};
+
+// *deg_done (may be null) is set when grad_deg was written.
 hipError_t launch_backward(const float* grad_out, const float* coupling, const float* radial,
                            InLayout L, const int32_t* dst32, const int32_t* rowptr,
                            const int32_t* perm, int64_t n_nodes, int64_t n_edges,
                            int64_t channels, float* grad_coupling, float* grad_radial, bool vec4,
-                           const float* norm, hipStream_t stream);
+                           NormGrad ng, bool* deg_done, hipStream_t stream);
 
 // Envelope gradient of the normalisation: grad_deg[n] (fp32, per node) from
-// grad_y, out and norm, then grad_env[e] = grad_deg[dst32[e]] (0 for dst32 < 0).
+// grad_y, out and norm unless deg_done, then grad_env[e] = grad_deg[dst32[e]]
+// (0 for dst32 < 0).
 hipError_t launch_norm_grad(const float* grad_y, const float* out, const float* norm,
                             const int32_t* dst32, int64_t n_nodes, int64_t n_edges,
-                            int64_t channels, float* grad_deg, float* grad_env,
+                            int64_t channels, float* grad_deg, float* grad_env, bool deg_done,
                             hipStream_t stream);
 
 // Small fill kernel (used instead of hipMemsetAsync so the calls stay

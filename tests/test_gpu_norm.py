@@ -202,3 +202,30 @@ def test_normalized_autograd(dev):
     _bitwise(rad.grad.cpu().numpy(), rgr, "autograd: grad_radial")
     _close(cpl.grad.cpu().numpy(), rgc, "autograd: grad_coupling")
     _close(env.grad.cpu().numpy(), rge, "autograd: grad_env")
+
+
+def test_normalized_backward_unaligned_out(dev):
+    """out at a 4-byte (not 16-byte) offset: the degree gradient then comes from
+    the separate per-node kernel instead of the backward's row staging."""
+    w = synthetic.custom("unaligned_out", 50, 4000, 32, seed=9501, envelope=True)
+    x = synthetic.make_inputs(w)
+    N, C = w.n_nodes, w.channels
+    t = {k: torch.from_numpy(x[k]).to(dev) for k in ("dst", "coupling", "radial", "env",
+                                                      "grad_out")}
+    csr = zs.zs_build_csr(t["dst"], N)
+    y, out, norm = zs.zs_forward_normalized(t["coupling"], t["radial"], t["env"], csr)
+    storage = torch.empty(N * 16 * C + 1, device=dev)
+    out_off = storage[1:].view(N, 16, C)
+    out_off.copy_(out)
+    assert out_off.data_ptr() % 16 == 4
+    say("[gpu] normalised backward with a 4-byte-offset out")
+    gc, gr, ge, gd = zs.zs_backward_normalized(t["grad_out"], out_off, norm, t["coupling"],
+                                               t["radial"], csr)
+    torch.cuda.synchronize()
+    ry, rout, rnorm = oracle.forward_norm(x["coupling"], x["radial"], x["env"], x["dst"], N)
+    rgc, rgr, rge = oracle.backward_norm(x["grad_out"], rout, rnorm, x["coupling"], x["radial"],
+                                         x["dst"])
+    _bitwise(gr.cpu().numpy(), rgr, "unaligned out: grad_radial")
+    _close(gc.cpu().numpy(), rgc, "unaligned out: grad_coupling")
+    _close(ge.cpu().numpy(), rge, "unaligned out: grad_env")
+    assert np.array_equal(_bits(gd.cpu().numpy()[x["dst"]]), _bits(ge.cpu().numpy()))
