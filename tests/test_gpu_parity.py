@@ -364,3 +364,59 @@ def test_strided_views(dev, label, N, E, C, slab, s0, band):
     assert np.array_equal(_bits(out.cpu().numpy()), _bits(ref_out)), f"{label}: forward"
     assert np.array_equal(_bits(gr.cpu().numpy()), _bits(ref_gr)), f"{label}: grad_radial"
     check_grad_coupling(gc.cpu().numpy(), ref_gc, f"{label}: grad_coupling")
+
+
+def test_hip_graph_capture_and_replay(dev):
+    """The whole step (asynchronous CSR build, forward, backward; also the
+    normalised pair) captured in one HIP graph and replayed several times, with
+    eager work and synchronisations between replays: every replay equals the
+    eager result bitwise.  None of the calls allocates, synchronises or
+    records a memset when given its buffers."""
+    w = synthetic.custom("graph", 300, 20000, 32, seed=4242, envelope=True)
+    x = synthetic.make_inputs(w)
+    N, E, C = w.n_nodes, w.n_edges, w.channels
+    say("[gpu] HIP graph capture of build + forward + backward")
+    t = {k: torch.from_numpy(x[k]).to(dev) for k in ("dst", "coupling", "radial", "env",
+                                                      "grad_out")}
+    csr = zs.Csr(torch.empty(N + 1, dtype=torch.int32, device=dev),
+                 torch.empty(E, dtype=torch.int32, device=dev),
+                 torch.empty(E, dtype=torch.int32, device=dev), N)
+    ws = torch.empty(zs.zs_csr_workspace_bytes(E, N), dtype=torch.uint8, device=dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.empty((N, 16, C), device=dev)
+    gc = torch.empty((E, 15), device=dev)
+    gr = torch.empty((E, 3, C), device=dev)
+
+    def step():
+        zs.zs_build_csr(t["dst"], N, workspace=ws, out=csr, bad_flag=flag)
+        zs.zs_forward(t["coupling"], t["radial"], csr, out=out)
+        zs.zs_backward(t["grad_out"], t["coupling"], t["radial"], csr, grad_coupling=gc,
+                       grad_radial=gr)
+        y, o, nrm = zs.zs_forward_normalized(t["coupling"], t["radial"], t["env"], csr)
+        grads = zs.zs_backward_normalized(t["grad_out"], o, nrm, t["coupling"], t["radial"], csr)
+        return [csr.rowptr, csr.perm, csr.dst32, out, gc, gr, y, o, nrm, *grads]
+
+    names = ("rowptr", "perm", "dst32", "out", "gc", "gr", "y", "out_n", "norm", "gc_n", "gr_n",
+             "genv", "gdeg")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        eager = [a.clone() for a in step()]   # warm-up on a side stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = step()
+    for rep in range(4):
+        for a in captured:
+            a.fill_(-7)   # eager work between replays, and a clobber the replay must undo
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(names, captured, eager):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"replay {rep}: {name}"
+        assert int(flag.item()) == 0
+    ref_out = oracle.forward(x["coupling"], x["radial"], x["dst"], N)
+    assert np.array_equal(_bits(out.cpu().numpy()), _bits(ref_out))
