@@ -251,6 +251,9 @@ def main() -> int:
                     help="run the workload's frame (same N, E, destinations and seed) with this "
                          "channel count instead of its own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the cache-flushed and normalised timings (so that counter runs "
+                         "see only the plain path's launches)")
     ap.add_argument("--inputs", default="contiguous", choices=["contiguous", "views"],
                     help="views: coupling read in place from a packed (E, 46) Wigner band and "
                          "radial features sliced from an (E, 5, C) tensor (strided entry points)")
@@ -383,9 +386,10 @@ def main() -> int:
         },
         "source_hash": {fam: kernel_source_hash(fam) for fam in KERNEL_SOURCES},
     }
-    rec["flushed"] = time_flushed(zs, torch, cpl, rad, g, csr, out, gc, gr, dev, nb,
-                                  min(args.steps, 20))
-    rec["normalized"] = time_normalized(zs, torch, cpl, rad, x, csr, dev, args.steps)
+    if not args.no_extras:
+        rec["flushed"] = time_flushed(zs, torch, cpl, rad, g, csr, out, gc, gr, dev, nb,
+                                      min(args.steps, 20))
+        rec["normalized"] = time_normalized(zs, torch, cpl, rad, x, csr, dev, args.steps)
     if args.calibrate_copy:
         src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst_copy = torch.empty_like(src)
