@@ -40,10 +40,9 @@
  *
  * Flat layouts (row-major, contiguous):
  *   coupling[e*15 + (r-1)], radial[(e*3 + (l-1))*C + c], out[(n*16 + r)*C + c].
- * The radial offset is the one pinned by the pages' review of the backward's
- * padded channel loads ("[P2] Mask the padded channels in backward's radial
- * loads"): a (777, 3, 40) radial tensor holds 93,240 floats and the last
- * edge's degree-3 row starts at float 93,200.
+ * The radial offset is the one pinned by the GIE page's review thread on
+ * masking the backward's padded channel loads: a (777, 3, 40) radial tensor
+ * holds 93,240 floats and the last edge's degree-3 row starts at float 93,200.
  *
  * Return values: 0 on success, -3 when a destination index is out of range.
  */
