@@ -476,7 +476,7 @@ struct BwdOccupancy {
 };
 
 // Largest number of work items a node is split into, and the edges per item
-// that a split aims at.  Measured (backward alone, same GPU, warm / flushed):
+// that a split aims at (both compile-time, so their divisions are cheap).  Measured (backward alone, same GPU, warm / flushed):
 // skewed degrees 157 -> 137 us, 1000-node frame 41 -> 36 us, 16384-node frame
 // 966 -> 932 us, uniform 4096-node frame 122 -> 123 us warm and 150 -> 146 us
 // cold, against no splitting.
@@ -487,6 +487,21 @@ constexpr int kBwdMaxParts = ZS_BWD_MAX_PARTS;
 #ifndef ZS_BWD_PART_EDGES
 #define ZS_BWD_PART_EDGES 40
 #endif
+constexpr uint32_t kBwdPartEdges = ZS_BWD_PART_EDGES;
+
+// floor(len * p / parts) for parts in 1..kBwdMaxParts, as 32-bit divisions by
+// constants.
+__device__ __attribute__((always_inline)) inline uint32_t split_point(uint32_t len, uint32_t p,
+                                                                      uint32_t parts) {
+    const uint64_t x = uint64_t(len) * p;
+    switch (parts) {
+        case 1: return uint32_t(x);
+        case 2: return uint32_t(x / 2);
+        case 3: return uint32_t(x / 3);
+        case 4: return uint32_t(x / 4);
+        default: return uint32_t(x / parts);
+    }
+}
 
 // FULL: C == NQ*VEC, every lane holds real channels (no channel masking).
 template <int NQ, int VEC, bool FULL>
@@ -495,8 +510,7 @@ void zs_bwd_staged_kernel(
     const float* __restrict__ grad_out, const float* __restrict__ coupling,
     const float* __restrict__ radial, InLayout L, const int32_t* __restrict__ rowptr,
     const int32_t* __restrict__ perm, int64_t n_nodes, int64_t n_edges, int64_t C,
-    float* __restrict__ grad_coupling, float* __restrict__ grad_radial, NormGrad ng,
-    int64_t part_edges) {
+    float* __restrict__ grad_coupling, float* __restrict__ grad_radial, NormGrad ng) {
     constexpr int EPW = 64 / NQ;
     constexpr int T = NQ * VEC;
     static_assert(T % 4 == 0, "the upstream rows are staged as float4");
@@ -512,27 +526,32 @@ void zs_bwd_staged_kernel(
     if (lane < EPW) wsh[lane * 16 + 15] = 0.0f;     // pad column, never fetched
 
     // Work item = (node, part), kBwdMaxParts items per node: a node of degree
-    // d is split into min(kBwdMaxParts, ceil(d / part_edges)) consecutive
+    // d is split into min(kBwdMaxParts, ceil(d / kBwdPartEdges)) consecutive
     // pieces (edges are independent here) and the items past that exit at
     // once.  High-degree nodes so become several work items of similar size,
     // which the dispatcher balances across the SIMDs.  Items are numbered
     // part-major (item = part * N + node): workgroups are handed to the XCDs
     // round-robin, so consecutive items must not share a part index.
     for (int64_t item = blockIdx.x; item < n_nodes * kBwdMaxParts; item += gridDim.x) {
-        const int64_t node = item % n_nodes;
-        const int part = int(item / n_nodes);
+        int64_t node = item;
+        int part = 0;
+        while (node >= n_nodes) {   // at most kBwdMaxParts - 1 steps
+            node -= n_nodes;
+            ++part;
+        }
         int64_t k0 = rowptr[node];
         int64_t k1 = rowptr[node + 1];
         k0 = k0 < 0 ? 0 : (k0 > n_edges ? n_edges : k0);
         k1 = k1 < k0 ? k0 : (k1 > n_edges ? n_edges : k1);
         {
-            const int64_t len = k1 - k0;
-            int64_t parts = (len + part_edges - 1) / part_edges;
+            // 32-bit arithmetic (CSR positions are int32) with constant divisors
+            const uint32_t len = uint32_t(k1 - k0);
+            uint32_t parts = len / kBwdPartEdges + (len % kBwdPartEdges != 0);
             parts = parts < 1 ? 1 : (parts > kBwdMaxParts ? kBwdMaxParts : parts);
-            if (part >= parts) continue;
-            const int64_t lo = k0 + len * part / parts;
-            k1 = k0 + len * (part + 1) / parts;
-            k0 = lo;
+            if (uint32_t(part) >= parts) continue;
+            const int64_t base = k0;
+            k0 = base + split_point(len, uint32_t(part), parts);
+            k1 = base + split_point(len, uint32_t(part) + 1, parts);
         }
         const bool deg = ng.grad_deg != nullptr && part == 0;   // also form the degree gradient
         if (k0 >= k1 && !deg) continue;
@@ -632,14 +651,13 @@ hipError_t launch_backward(const float* grad_out, const float* coupling, const f
         if (channels == (NQ) * (VEC))                                                            \
             zs_bwd_staged_kernel<NQ, VEC, true><<<gxp, 64, 0, stream>>>(                         \
                 grad_out, coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels,         \
-                grad_coupling, grad_radial, ng, part_edges);                                          \
+                grad_coupling, grad_radial, ng);                                          \
         else                                                                                     \
             zs_bwd_staged_kernel<NQ, VEC, false><<<gxp, 64, 0, stream>>>(                        \
                 grad_out, coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels,         \
-                grad_coupling, grad_radial, ng, part_edges);                                          \
+                grad_coupling, grad_radial, ng);                                          \
         if (deg_done) *deg_done = ng.grad_deg != nullptr;                                        \
     } while (0)
-    const int64_t part_edges = ZS_BWD_PART_EDGES;
     const int64_t items = n_nodes * kBwdMaxParts;
     const unsigned gxp = unsigned(items < kGridCap ? items : kGridCap);
     int nq = 0, vec = 0;
