@@ -429,11 +429,16 @@ void launch_staged(const float* coupling, const float* radial, InLayout L, const
             coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
 }
 
-// Edges per batch.  Measured at the 4096-node frame: 4 beats 8 (and 16, and 2)
-// at every channel count, warm and with cold caches (C = 32: 55 vs 58 us).
-#ifndef ZS_FWD_BATCH
-#define ZS_FWD_BATCH 4
-#endif
+// Edges per batch, from the number of wavefronts the launch provides.  With at
+// least 4 per SIMD (4096), other wavefronts hide each one's latency and 4 is
+// best (4096-node frame, C = 32: 55 us, 8 edges 57 us, 16 edges slower).  With
+// fewer, a wavefront's own batches must keep its loads in flight (1000-node
+// frame: 34 us at 4, 26 us at 8, 23 us at 16).  Batches above 4 edges are
+// used at <= 4 channels per lane, to bound the registers.
+int forward_batch(int64_t waves, int vec) {
+    if (vec > 4 || waves >= 4096) return 4;
+    return waves >= 2048 ? 8 : 16;
+}
 
 // Channel tiling of the staged forward: one tile of VEC = ceil(C / 8)
 // channels per lane up to 64 channels; beyond that, tiles of 64 channels, so
@@ -455,16 +460,26 @@ hipError_t launch_forward(const float* coupling, const float* radial, InLayout L
 #define ZS_FWD_STAGED(V, BB)                                                                     \
     launch_staged<V, BB>(coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio, \
                          gx, stream)
-        switch (forward_tile_vec(channels)) {
-            case 1: ZS_FWD_STAGED(1, ZS_FWD_BATCH); break;
-            case 2: ZS_FWD_STAGED(2, ZS_FWD_BATCH); break;
-            case 3: ZS_FWD_STAGED(3, ZS_FWD_BATCH); break;
-            case 4: ZS_FWD_STAGED(4, ZS_FWD_BATCH); break;
-            case 5: ZS_FWD_STAGED(5, ZS_FWD_BATCH); break;
-            case 6: ZS_FWD_STAGED(6, ZS_FWD_BATCH); break;
-            case 7: ZS_FWD_STAGED(7, ZS_FWD_BATCH); break;
-            default: ZS_FWD_STAGED(8, ZS_FWD_BATCH); break;
+#define ZS_FWD_STAGED_B(V)                         \
+    switch (batch) {                               \
+        case 16: ZS_FWD_STAGED(V, 16); break;      \
+        case 8: ZS_FWD_STAGED(V, 8); break;        \
+        default: ZS_FWD_STAGED(V, 4); break;       \
+    }
+        const int vec = forward_tile_vec(channels);
+        const int64_t tiles = (channels + 8 * vec - 1) / (8 * vec);
+        const int batch = forward_batch(int64_t(gx) * tiles, vec);
+        switch (vec) {
+            case 1: ZS_FWD_STAGED_B(1); break;
+            case 2: ZS_FWD_STAGED_B(2); break;
+            case 3: ZS_FWD_STAGED_B(3); break;
+            case 4: ZS_FWD_STAGED_B(4); break;
+            case 5: ZS_FWD_STAGED(5, 4); break;
+            case 6: ZS_FWD_STAGED(6, 4); break;
+            case 7: ZS_FWD_STAGED(7, 4); break;
+            default: ZS_FWD_STAGED(8, 4); break;
         }
+#undef ZS_FWD_STAGED_B
 #undef ZS_FWD_STAGED
     } else {
         constexpr int NQ = 16, VEC = 1;

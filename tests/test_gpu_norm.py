@@ -118,6 +118,7 @@ NORM_CASES = [
     ("c33_scalar", 8, 400, 33, "uniform"),
     ("one_edge", 5, 1, 32, "uniform"),
     ("hub", 3, 5000, 32, "uniform"),
+    ("n2500_batch8", 2500, 40000, 32, "uniform"),
 ]
 
 

@@ -168,7 +168,8 @@ EDGE_CASES = [
     ("c260", 9, 300, 260, "uniform"),
     ("c1024", 3, 70, 1024, "uniform"),
     ("skew_small", 200, 9000, 32, "skewed_small"),
-    ("nodes_20000", 20000, 40000, 8, "uniform"),      # global-bin CSR path (N > 16384)
+    ("nodes_20000", 20000, 40000, 8, "uniform"),      # many buckets; 4-edge forward batches
+    ("nodes_3000", 3000, 90000, 32, "uniform"),       # 8-edge forward batches (2048..4095 waves)
 ]
 
 
