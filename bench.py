@@ -6,8 +6,11 @@ is already resident in HBM: the stable destination CSR build, the fused
 forward and the fused backward (zs_build_csr in its asynchronous mode, so the
 step has no host synchronization, then zs_forward and zs_backward), all on
 torch's current stream.  W warmup steps, then exactly K timed steps between
-two device synchronizations.  Each kernel call is bracketed by HIP events
-recorded on the same stream, which give the per-call durations.
+two device synchronizations.  HIP events recorded on the same stream bracket
+the build and the forward + backward pair of every timed step; K more steps
+with an extra event between forward and backward give the per-call durations
+(an event between the two calls costs a few microseconds of its own, so it is
+kept out of the pair's timing).
 
 The JSON line's ``value`` is the algorithmic HBM throughput of forward +
 backward (GB/s): the unique bytes those two calls must move, divided by their
@@ -305,14 +308,17 @@ def main() -> int:
     gc = torch.empty((E, 15), device=dev)
     gr = torch.empty((E, 3, C), device=dev)
 
-    def step(evs=None):
+    def step(evs=None, split=False):
+        """One step.  evs: [before build, before forward, between (split only),
+        after backward]; the forward + backward time is the span of one event
+        pair (an event between the two calls adds a few microseconds of its own)."""
         if evs is not None:
             evs[0].record()
         zs.zs_build_csr(dst, N, workspace=ws, out=csr, bad_flag=flag)
         if evs is not None:
             evs[1].record()
         zs.zs_forward(cpl, rad, csr, out=out)
-        if evs is not None:
+        if evs is not None and split:
             evs[2].record()
         zs.zs_backward(g, cpl, rad, csr, grad_coupling=gc, grad_radial=gr)
         if evs is not None:
@@ -335,12 +341,20 @@ def main() -> int:
         raise RuntimeError("destination index out of range in the synthetic input")
 
     build_ms = [ev[0].elapsed_time(ev[1]) for ev in events]
-    fwd_ms = [ev[1].elapsed_time(ev[2]) for ev in events]
-    bwd_ms = [ev[2].elapsed_time(ev[3]) for ev in events]
+    fb_ms = [ev[1].elapsed_time(ev[3]) for ev in events]
+    # per-call split (for the per-kernel figures and the roofline): the same steps
+    # again with an event between forward and backward
+    split_events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                    for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(split_events[i], split=True)
+    torch.cuda.synchronize()
+    fwd_ms = [ev[1].elapsed_time(ev[2]) for ev in split_events]
+    bwd_ms = [ev[2].elapsed_time(ev[3]) for ev in split_events]
     mean = statistics.fmean
     nb = algorithmic_bytes(E, N, C)
     fwd_us, bwd_us, build_us = mean(fwd_ms) * 1e3, mean(bwd_ms) * 1e3, mean(build_ms) * 1e3
-    fb_us = fwd_us + bwd_us
+    fb_us = mean(fb_ms) * 1e3
     gbs = (nb["fwd"] + nb["bwd"]) / (fb_us * 1e-6) / 1e9
     bwd_gbs = nb["bwd"] / (bwd_us * 1e-6) / 1e9
     # the committed counter summary covers the headline frame with contiguous inputs only
@@ -369,7 +383,7 @@ def main() -> int:
         "fwd_us": round(fwd_us, 2),
         "bwd_us": round(bwd_us, 2),
         "build_us": round(build_us, 2),
-        "fwd_bwd_us_median": round((statistics.median(fwd_ms) + statistics.median(bwd_ms)) * 1e3, 2),
+        "fwd_bwd_us_median": round(statistics.median(fb_ms) * 1e3, 2),
         "edges_per_s": round(E / (fb_us * 1e-6), 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": nb,
