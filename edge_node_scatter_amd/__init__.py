@@ -135,8 +135,8 @@ def _edge_views(coupling: torch.Tensor, radial: torch.Tensor):
 def coupling_from_band(band: torch.Tensor, m0_offset: int = 15) -> torch.Tensor:
     """The zonal coupling (E, 15) as a view of a packed (E, 46) Wigner band.
 
-    The band stores, per edge, three segments (the band page's "three
-    structural rows per degree block"): two of 15 entries and the m = 0
+    The band stores, per edge, three segments (the band page keeps three
+    structural rows of each degree block): two of 15 entries and the m = 0
     segment of 16 entries (rows 0..15, row 0 being the l = 0 block).  The
     pages do not print the segment order; the default m0_offset = 15 reads
     them in increasing m (m = -1, 0, +1), so the coupling of rows 1..15 is
