@@ -1,0 +1,121 @@
+"""Host-side logic (CPU only): the seeded workload recipes and bench.py's
+bookkeeping (algorithmic bytes, counter summaries, the one-GPU contract)."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+import synthetic
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("name", ["tiny", "n1000", "headline", "skewed"])
+def test_workload_sizes_and_ranges(name):
+    w = synthetic.WORKLOADS[name]
+    x = synthetic.make_inputs(w)
+    E, N, C = w.n_edges, w.n_nodes, w.channels
+    assert x["dst"].shape == (E,) and x["dst"].dtype == np.int64
+    assert x["dst"].min() >= 0 and x["dst"].max() < N
+    assert x["coupling"].shape == (E, 15) and x["coupling"].dtype == np.float32
+    assert x["radial"].shape == (E, 3, C) and x["radial"].dtype == np.float32
+    assert x["grad_out"].shape == (N, 16, C)
+    assert x["env"].shape == (E,) and np.all((x["env"] >= 0) & (x["env"] < 1))
+    assert np.all(np.abs(x["coupling"]) <= 1.0)
+    if w.envelope:   # coupling = U(-1, 1) * env, so |coupling| <= env
+        assert np.all(np.abs(x["coupling"]) <= x["env"][:, None] + 1e-7)
+
+
+def test_headline_degrees_near_constant():
+    """647170 = 4096 * 158 + 2: all nodes of degree 158 but two of 159."""
+    w = synthetic.WORKLOADS["headline"]
+    deg = np.bincount(synthetic.make_dst(w), minlength=w.n_nodes)
+    assert deg.sum() == 647170
+    assert sorted(set(deg.tolist())) == [158, 159] and np.count_nonzero(deg == 159) == 2
+
+
+def test_skewed_degrees():
+    w = synthetic.WORKLOADS["skewed"]
+    deg = np.bincount(synthetic.make_dst(w), minlength=w.n_nodes)
+    assert deg.sum() == w.n_edges
+    assert np.count_nonzero(deg == 0) >= 64
+    live = np.sort(deg[deg > 0])
+    lo, hi = live[: len(live) // 2], live[len(live) // 2:]
+    assert 30 < lo.mean() < 50 and 250 < hi.mean() < 300   # Poisson(40) / Poisson(275) halves
+
+
+def test_edge_order_is_shuffled():
+    """Destinations are not grouped: consecutive edges rarely share a node."""
+    d = synthetic.make_dst(synthetic.WORKLOADS["headline"])
+    assert np.mean(d[1:] == d[:-1]) < 0.01
+
+
+def test_inputs_deterministic_and_streams_independent():
+    w = synthetic.WORKLOADS["tiny"]
+    a, b = synthetic.make_inputs(w), synthetic.make_inputs(w)
+    for k in ("dst", "coupling", "radial", "grad_out", "env"):
+        assert np.array_equal(a[k], b[k]), k
+    # a different channel count changes radial but no other tensor's values
+    w2 = synthetic.custom("tiny_c8", w.n_nodes, w.n_edges, 8, w.seed, w.dst_kind, w.envelope)
+    c = synthetic.make_inputs(w2)
+    for k in ("dst", "coupling", "env"):
+        assert np.array_equal(a[k], c[k]), k
+
+
+def test_algorithmic_bytes_match_the_published_arithmetic():
+    """Headline shape: forward 298.3 MB, backward 585.7 MB, together 884.0 MB;
+    at 8 TB/s that is 110.5 us, and 60 % of peak is at most 184.2 us."""
+    nb = bench.algorithmic_bytes(647170, 4096, 32)
+    assert round(nb["fwd"] / 1e6, 1) == 298.3
+    assert round(nb["bwd"] / 1e6, 1) == 585.7
+    total = nb["fwd"] + nb["bwd"]
+    assert round(total / 1e6, 1) == 884.0
+    assert round(total / 8e12 * 1e6, 1) == 110.5
+    assert round(total / (0.6 * 8e12) * 1e6, 1) == 184.2
+    large = bench.algorithmic_bytes(2600000, 16384, 64)
+    assert round((large["fwd"] + large["bwd"]) / 1e6, 1) == 6613.5
+    nn = bench.algorithmic_bytes_normalized(647170, 4096, 32)
+    assert nn["fwd"] - nb["fwd"] == 4 * 647170 + 4096 * (16 * 32 * 4 + 4)
+    assert nn["bwd"] - nb["bwd"] == 4096 * (15 * 32 * 4 + 8) + 8 * 647170
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for name, value in rows:
+            wr.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_write_traffic_scales_by_the_copy(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    kib = bench.COPY_CALIBRATION_BYTES / 1024
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    bwd = "void zs::(anonymous namespace)::zs_bwd_staged_kernel<8, 4, true>(float const*)"
+    _counter_csv(fetch, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", kib / 2),   # reads half
+                                       (bwd, 1000.0), (bwd, 1200.0)])
+    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", kib), (bwd, 500.0)])
+    out = bench.write_traffic(str(fetch), str(write))
+    assert out["fetch_scale"] == pytest.approx(2.0) and out["write_scale"] == pytest.approx(1.0)
+    k = out["kernels"]["zs_bwd_staged_kernel"]
+    assert k["fetch_bytes"] == round(1100.0 * 1024 * 2.0)
+    assert k["hbm_bytes_per_launch"] == round(1100.0 * 1024 * 2.0 + 500.0 * 1024)
+    assert k["source_hash"] == bench.kernel_source_hash("bwd")
+    assert bench.load_traffic("zs_bwd_staged_kernel") == k["hbm_bytes_per_launch"]
+    # a record taken on other sources is not reported
+    k["source_hash"] = "0" * 16
+    with open(bench.TRAFFIC_FILE, "w") as f:
+        json.dump(out, f)
+    assert bench.load_traffic("zs_bwd_staged_kernel") is None
+
+
+def test_bench_refuses_several_gpus():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
