@@ -114,7 +114,7 @@ def make_dst(w: Workload) -> np.ndarray:
     return dst[_rng(w.seed, _TAG_SHUFFLE).permutation(w.n_edges)]
 
 
-def make_inputs(w: Workload | str, with_grad: bool = True) -> dict:
+def make_inputs(w: Workload | str, with_grad: bool = True, tiled_radial: bool = False) -> dict:
     """All operator inputs for workload ``w`` as contiguous numpy arrays.
 
     dst      (E,)          int64
@@ -122,6 +122,9 @@ def make_inputs(w: Workload | str, with_grad: bool = True) -> dict:
     coupling (E, 15)       float32, U(-1,1) (times env when the workload has one)
     radial   (E, 3, C)     float32, N(0,1)
     grad_out (N, 16, C)    float32, N(0,1)   (upstream gradient of the output)
+
+    With ``tiled_radial`` the radial tensor is not materialised: ``radial_pool``
+    holds the pool it tiles (see ``radial_pool``) instead.
     """
     if isinstance(w, str):
         w = WORKLOADS[w]
@@ -133,7 +136,11 @@ def make_inputs(w: Workload | str, with_grad: bool = True) -> dict:
         cpl = cpl * env[:, None]
     out["coupling"] = np.ascontiguousarray(cpl.astype(np.float32))
     out["env"] = env.astype(np.float32)
-    out["radial"] = _rng(w.seed, _TAG_RADIAL).standard_normal(size=(E, SLOTS, C), dtype=np.float32)
+    if tiled_radial:
+        out["radial_pool"] = radial_pool(w)
+    else:
+        out["radial"] = _rng(w.seed, _TAG_RADIAL).standard_normal(size=(E, SLOTS, C),
+                                                                 dtype=np.float32)
     if with_grad:
         out["grad_out"] = _rng(w.seed, _TAG_GRAD).standard_normal(size=(N, ROWS, C), dtype=np.float32)
     return out
@@ -152,3 +159,23 @@ def fingerprint(arrays: dict) -> dict:
         if isinstance(v, np.ndarray):
             fp[k] = hashlib.blake2b(np.ascontiguousarray(v).view(np.uint8), digest_size=8).hexdigest()
     return fp
+
+
+# Inputs past 2^31 elements.  Drawing billions of normals on the host takes
+# minutes, so the radial tensor of such a workload is a seeded N(0,1) pool of
+# prime length tiled over the flat (E, 3, C) array: element k is pool[k % P].
+# Because P is prime, 2^32 is not a multiple of P, so an offset that wrapped
+# at 32 bits would read a different pool entry.
+RADIAL_POOL_LEN = 16777259   # prime, just above 2^24
+
+
+def radial_pool(w: Workload, length: int = RADIAL_POOL_LEN) -> np.ndarray:
+    """The seeded pool (float32, N(0,1)) a tiled radial tensor repeats."""
+    return _rng(w.seed, _TAG_RADIAL).standard_normal(size=length, dtype=np.float32)
+
+
+def tiled_radial_rows(pool: np.ndarray, edges: np.ndarray, channels: int) -> np.ndarray:
+    """Rows radial[edges] (len(edges), 3, C) of the tiled radial tensor."""
+    per_edge = SLOTS * channels
+    k = np.asarray(edges, dtype=np.int64)[:, None] * per_edge + np.arange(per_edge, dtype=np.int64)
+    return pool[k % pool.shape[0]].reshape(-1, SLOTS, channels)

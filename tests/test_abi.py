@@ -168,3 +168,24 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         zs.zs_build_csr(torch.zeros(3, dtype=torch.int64), 4)
+
+
+def test_c_client_links_against_the_header(c_client, tmp_path):
+    """The header compiles as C11 with -Wall -Werror, and a plain C program
+    links against libzs.so alone for every call it makes."""
+    out = subprocess.check_output(["nm", "-u", c_client], text=True)
+    undefined = {line.split()[-1] for line in out.splitlines()}
+    for name in ("zs_status_string", "zs_csr_workspace_bytes", "zs_build_csr", "zs_forward",
+                 "zs_backward"):
+        assert name in undefined, name
+    # argument and file errors are handled before any HIP call
+    r = subprocess.run([c_client], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
+    r = subprocess.run([c_client, str(tmp_path / "missing.bin"), str(tmp_path / "o.bin")],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1
+    short = tmp_path / "short.bin"
+    short.write_bytes(b"\x01\x00")
+    r = subprocess.run([c_client, str(short), str(tmp_path / "o.bin")],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "short header" in r.stderr

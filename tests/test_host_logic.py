@@ -119,3 +119,39 @@ def test_bench_refuses_several_gpus():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_tiled_radial_rows_match_the_materialised_tiling():
+    """Rows picked by formula equal the rows of the flat tiled array, which is
+    how the device builds it (a 1-D repeat of the pool, then a view)."""
+    w = synthetic.custom("tiled", 7, 50, 5, seed=3)
+    pool = synthetic.radial_pool(w, length=101)        # prime, shorter than E * 3 * C
+    flat = np.tile(pool, -(-50 * 3 * 5 // 101))[: 50 * 3 * 5].reshape(50, 3, 5)
+    edges = np.array([0, 1, 6, 7, 33, 49])
+    assert np.array_equal(synthetic.tiled_radial_rows(pool, edges, 5), flat[edges])
+    big = synthetic.radial_pool(w)
+    assert big.shape == (synthetic.RADIAL_POOL_LEN,) and big.dtype == np.float32
+    assert abs(float(big.mean())) < 1e-3 and abs(float(big.std()) - 1.0) < 1e-3
+    assert (2 ** 32) % synthetic.RADIAL_POOL_LEN != 0
+
+
+def test_forward_rows_of_a_node_subset_need_only_their_edges():
+    """The sampled parity check at sizes past 2^31 elements runs the oracle on
+    just the sampled nodes' edges (increasing edge id, destinations renumbered);
+    on a small frame that equals the full oracle's rows bit for bit, and the
+    per-edge backward of a subset equals the full backward's rows."""
+    import oracle
+    w = synthetic.custom("subset", 40, 3000, 8, seed=11, envelope=True)
+    x = synthetic.make_inputs(w)
+    full = oracle.forward(x["coupling"], x["radial"], x["dst"], 40)
+    nodes = np.array([0, 3, 17, 39])
+    sub = np.flatnonzero(np.isin(x["dst"], nodes))
+    part = oracle.forward(x["coupling"][sub], x["radial"][sub],
+                          np.searchsorted(nodes, x["dst"][sub]), len(nodes))
+    assert np.array_equal(part.view(np.uint32), full[nodes].view(np.uint32))
+    gc, gr = oracle.backward(x["grad_out"], x["coupling"], x["radial"], x["dst"])
+    edges = np.array([0, 5, 2999])
+    gc_s, gr_s = oracle.backward(x["grad_out"], x["coupling"][edges], x["radial"][edges],
+                                 x["dst"][edges])
+    assert np.array_equal(gc_s.view(np.uint32), gc[edges].view(np.uint32))
+    assert np.array_equal(gr_s.view(np.uint32), gr[edges].view(np.uint32))
