@@ -633,13 +633,12 @@ bool backward_layout(int64_t C, int& nq, int& vec) {
 }  // namespace
 
 hipError_t launch_backward(const float* grad_out, const float* coupling, const float* radial,
-                           InLayout L, const int32_t* dst32, const int32_t* rowptr,
-                           const int32_t* perm, int64_t n_nodes, int64_t n_edges,
+                           InLayout L, const int32_t* rowptr, const int32_t* perm,
+                           int64_t n_nodes, int64_t n_edges,
                            int64_t channels, float* grad_coupling, float* grad_radial, bool vec4,
                            NormGrad ng, bool* deg_done, hipStream_t stream) {
     const float* norm = ng.norm;
     if (deg_done) *deg_done = false;
-    (void)dst32;   // this traversal is CSR-major; dst32 serves edge-major variants
     constexpr int64_t kGridCap = 1 << 20;
     const unsigned gx = unsigned(n_nodes < kGridCap ? n_nodes : kGridCap);
 #define ZS_BWD_LAUNCH(VEC, NQ, GREG)                                                            \

@@ -6,7 +6,13 @@
 // (N, 16, C) layout with a zero scalar row; the (E, 15, C) message surface is
 // never formed.
 //
-// Mapping (one 64-lane wavefront per node and channel tile):
+// Three kernels, chosen per launch: zs_fwd_staged_kernel (one wavefront per
+// node and channel tile, C % 4 == 0, aligned), zs_fwd_slot_kernel (three
+// wavefronts per node and tile, one per radial slot, for launches with few
+// nodes) and zs_fwd_kernel (any C and alignment).  All three accumulate the
+// same products in the same order, so their results are bitwise equal.
+//
+// Mapping of zs_fwd_kernel (one 64-lane wavefront per node and channel tile):
 //   lane = j * NQ + q.  q picks VEC consecutive channels (tile width NQ*VEC),
 //   j picks a slot of RPS consecutive padded rows (rows j*RPS+1 .. j*RPS+RPS;
 //   the one past row 15 stands for the scalar row 0 and is written as +0).
@@ -416,6 +422,182 @@ __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restri
     }
 }
 
+// ---------------------------------------------------------------------------
+// Slot-split forward: a workgroup of three wavefronts per (node, channel tile
+// of T = 8*VEC channels).  Wavefront s accumulates the rows of degree
+// l = s + 1 (rows l*l .. l*l + 2l, 2l + 1 of them), so it reads only radial
+// slot s of each edge (whole 128-byte lines at C = 32) and coupling columns
+// l*l - 1 .. l*l + 2l - 1.  Lane = j*8 + q owns row l*l + j (j < 2l + 1) and
+// channels q*VEC .. q*VEC+VEC-1 of the tile.  Each wavefront walks the node's
+// edges in CSR order with the staged kernel's pipeline (perm entries two
+// batches ahead, data one batch ahead, unconditional loads, LDS staging);
+// the three wavefronts share the CU's caches for the node's perm entries and
+// coupling lines and need no barrier: each stages into its own LDS slice.
+// Accumulation order and arithmetic are those of zs_fwd_kernel, so results
+// are bitwise those of the other forward kernels.
+// ---------------------------------------------------------------------------
+template <int VEC, int B>
+struct SlotShape {
+    static constexpr int T = 8 * VEC;          // channels per tile
+    static constexpr int F4 = T / 4;           // float4 per slot row of a tile
+    static constexpr int RAD = B * F4;         // radial float4 per batch
+    static constexpr int RV = (RAD + 63) / 64;
+    static constexpr int CW = B * 8;           // coupling floats per batch: 8 per edge
+    static constexpr int CV = (CW + 63) / 64;
+};
+
+template <int VEC, int B, bool NORM>
+__global__ __launch_bounds__(192) void zs_fwd_slot_kernel(const float* __restrict__ coupling,
+                                                          const float* __restrict__ radial,
+                                                          InLayout L,
+                                                          const int32_t* __restrict__ rowptr,
+                                                          const int32_t* __restrict__ perm,
+                                                          int64_t n_nodes, int64_t n_edges,
+                                                          int64_t C, float* __restrict__ out,
+                                                          NormIO nio) {
+    using S = SlotShape<VEC, B>;
+    static_assert(B <= 64, "one perm entry per lane");
+    __shared__ float4 rsh_all[kSlots][S::RAD];
+    __shared__ float csh_all[kSlots][S::CW];
+
+    const int s = threadIdx.x >> 6;            // slot of this wavefront
+    const int lane = threadIdx.x & 63;
+    const int l = s + 1;
+    const int r0 = l * l;                      // first row of the slot
+    const int nr = 2 * l + 1;                  // rows of the slot
+    const int q = lane & 7;
+    const int j = lane >> 3;
+    float4* rsh = rsh_all[s];
+    float* csh = csh_all[s];
+    const int64_t cbase = int64_t(blockIdx.y) * S::T;
+    const int64_t c0 = cbase + q * VEC;
+    const int n_valid = c0 >= C ? 0 : (C - c0 < VEC ? int(C - c0) : VEC);
+    const int64_t slot_off = int64_t(s) * L.rad_slot;
+
+    for (int64_t node = blockIdx.x; node < n_nodes; node += gridDim.x) {
+        int64_t k0 = rowptr[node];
+        int64_t k1 = rowptr[node + 1];
+        k0 = k0 < 0 ? 0 : (k0 > n_edges ? n_edges : k0);
+        k1 = k1 < k0 ? k0 : (k1 > n_edges ? n_edges : k1);
+        const int64_t nb = (k1 - k0 + B - 1) / B;
+
+        float acc[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
+        float deg = 0.0f;
+
+        // Loads of one batch: radial float4 f = i*64 + lane is batch edge
+        // f / F4, float4 f % F4 of the tile's slot row; coupling float
+        // idx = i*64 + lane is batch edge idx / 8, column idx % 8 of the slot
+        // (column 7, never a row of the slot, carries the envelope factor
+        // with NORM).  Absent edges, channels and columns read a valid
+        // substitute (edge 0, the tile's first channel, the slot's first
+        // column) that is never used.
+        auto fetch = [&](float4 (&rr)[S::RV], float (&ww)[S::CV], int pe) {
+#pragma unroll
+            for (int i = 0; i < S::RV; ++i) {
+                const int f = i * 64 + lane;
+                const int e = __shfl(pe, f < S::RAD ? f / S::F4 : 0, 64);
+                const int64_t es = e >= 0 ? e : 0;
+                const int64_t ch = cbase + (f % S::F4) * 4;
+                const int64_t cs = ch < C ? ch : cbase;
+                rr[i] = load_stream4<ZS_FWD_NT != 0>(radial + es * L.rad_edge + slot_off + cs);
+            }
+#pragma unroll
+            for (int i = 0; i < S::CV; ++i) {
+                const int idx = i * 64 + lane;
+                const int b = idx < S::CW ? idx >> 3 : 0;
+                const int col = idx & 7;
+                const int e = __shfl(pe, b, 64);
+                const int64_t es = e >= 0 ? e : 0;
+                const bool in_env = NORM && col == 7;
+                ww[i] = in_env ? nio.env[es]
+                               : coupling[es * L.cpl_edge + (r0 - 1) + (col < nr ? col : 0)];
+            }
+        };
+        auto stage_accumulate = [&](const float4 (&rr)[S::RV], const float (&ww)[S::CV],
+                                    int cnt) {
+#pragma unroll
+            for (int i = 0; i < S::RV; ++i)
+                if (S::RAD % 64 == 0 || i * 64 + lane < S::RAD) rsh[i * 64 + lane] = rr[i];
+#pragma unroll
+            for (int i = 0; i < S::CV; ++i)
+                if (S::CW % 64 == 0 || i * 64 + lane < S::CW) csh[i * 64 + lane] = ww[i];
+            const float* rf = reinterpret_cast<const float*>(rsh);
+            const int jw = j < nr ? j : 0;
+            auto edge = [&](int b) {
+                if (NORM) deg = deg + csh[b * 8 + 7];
+                float x[VEC];
+                lds_read<VEC>(rf + b * S::T + q * VEC, x);
+                const float w = csh[b * 8 + jw];
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    const float m = w * x[v];
+                    acc[v] = acc[v] + m;
+                }
+            };
+            if (cnt == B) {
+#pragma unroll
+                for (int b = 0; b < B; ++b) edge(b);
+            } else {
+                for (int b = 0; b < cnt; ++b) edge(b);
+            }
+        };
+        auto batch_count = [k0, k1](int64_t t) {
+            const int64_t kb = k0 + t * B;
+            return int(k1 - kb < B ? k1 - kb : B);
+        };
+
+        if (nb > 0) {
+            float4 RA[S::RV], RB[S::RV];
+            float WA[S::CV], WB[S::CV];
+            PermRaw pA = perm_issue(perm, k0, k1, lane, B);
+            PermRaw pB = perm_issue(perm, k0 + B, k1, lane, B);
+            fetch(RA, WA, perm_resolve(pA, n_edges));
+            for (int64_t t = 0; t < nb; t += 2) {
+                const PermRaw pN = perm_issue(perm, k0 + (t + 2) * B, k1, lane, B);
+                fetch(RB, WB, perm_resolve(pB, n_edges));
+                stage_accumulate(RA, WA, batch_count(t));
+                if (t + 1 >= nb) break;
+                pB = perm_issue(perm, k0 + (t + 3) * B, k1, lane, B);
+                fetch(RA, WA, perm_resolve(pN, n_edges));
+                stage_accumulate(RB, WB, batch_count(t + 1));
+            }
+        }
+
+        float zero[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) zero[v] = 0.0f;
+        const int64_t row_off = node * kRows * C + c0;
+        if (NORM) {
+            const float nrm = deg > 0.0f ? 1.0f / sqrtf(deg) : 0.0f;
+            if (s == 0 && lane == 0 && blockIdx.y == 0) nio.norm[node] = nrm;
+            float y[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) y[v] = acc[v] * nrm;
+            if (j < nr) row_store<VEC>(nio.y + row_off + int64_t(r0 + j) * C, y, n_valid);
+            else if (s == 0 && j == nr) row_store<VEC>(nio.y + row_off, zero, n_valid);
+        }
+        if (!NORM || out != nullptr) {
+            if (j < nr) row_store<VEC>(out + row_off + int64_t(r0 + j) * C, acc, n_valid);
+            else if (s == 0 && j == nr) row_store<VEC>(out + row_off, zero, n_valid);
+        }
+    }
+}
+
+template <int VEC, int B>
+void launch_slot(const float* coupling, const float* radial, InLayout L, const int32_t* rowptr,
+                 const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels,
+                 float* out, NormIO nio, unsigned gx, hipStream_t stream) {
+    const unsigned gy = unsigned((channels + 8 * VEC - 1) / (8 * VEC));
+    if (nio.y != nullptr)
+        zs_fwd_slot_kernel<VEC, B, true><<<dim3(gx, gy), 192, 0, stream>>>(
+            coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
+    else
+        zs_fwd_slot_kernel<VEC, B, false><<<dim3(gx, gy), 192, 0, stream>>>(
+            coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
+}
+
 template <int VEC, int B>
 void launch_staged(const float* coupling, const float* radial, InLayout L, const int32_t* rowptr,
                    const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels,
@@ -429,15 +611,29 @@ void launch_staged(const float* coupling, const float* radial, InLayout L, const
             coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
 }
 
-// Edges per batch, from the number of wavefronts the launch provides.  With at
-// least 4 per SIMD (4096), other wavefronts hide each one's latency and 4 is
-// best (4096-node frame, C = 32: 55 us, 8 edges 57 us, 16 edges slower).  With
-// fewer, a wavefront's own batches must keep its loads in flight (1000-node
-// frame: 34 us at 4, 26 us at 8, 23 us at 16).  Batches above 4 edges are
-// used at <= 4 channels per lane, to bound the registers.
+// Edges per batch of the staged kernel, from the number of wavefronts the
+// launch provides.  With at least 4 per SIMD (4096), other wavefronts hide
+// each one's latency and 4 is best (4096-node frame, C = 32: 55 us, 8 edges
+// 57 us, 16 edges slower).  With fewer, a wavefront's own batches must keep
+// its loads in flight (8 edges; smaller launches go to the slot-split kernel,
+// below).  Batches above 4 edges are used at <= 4 channels per lane, to bound
+// the registers.
 int forward_batch(int64_t waves, int vec) {
-    if (vec > 4 || waves >= 4096) return 4;
-    return waves >= 2048 ? 8 : 16;
+    return (vec > 4 || waves >= 4096) ? 4 : 8;
+}
+
+// When a frame gives the one-wavefront-per-tile kernel too few wavefronts to
+// keep the memory system busy, the slot-split kernel's three per tile win:
+// measured warm on one GPU at 158 edges per node, C = 32: 500 nodes
+// 21.1 -> 14.8 us, 1000 nodes 22.7 -> 18.3 us (16-edge batches), 1500 nodes
+// 27.1 -> 24.9 us, 2000 nodes 33.6 -> 31.6 us (8-edge batches), 2500 nodes
+// and more slower (39.4 -> 40.6 us); C = 64, 1000 nodes 41.2 -> 29.0 us,
+// 2000 nodes slower.  Returns the slot kernel's batch, or 0 for the staged
+// kernel.
+int forward_slot_batch(int64_t waves, int vec) {
+    if (waves < 1280) return vec > 4 ? 8 : 16;
+    if (vec <= 4 && waves < 2048) return 8;
+    return 0;
 }
 
 // Channel tiling of the staged forward: one tile of VEC = ceil(C / 8)
@@ -462,13 +658,36 @@ hipError_t launch_forward(const float* coupling, const float* radial, InLayout L
                          gx, stream)
 #define ZS_FWD_STAGED_B(V)                         \
     switch (batch) {                               \
-        case 16: ZS_FWD_STAGED(V, 16); break;      \
         case 8: ZS_FWD_STAGED(V, 8); break;        \
         default: ZS_FWD_STAGED(V, 4); break;       \
     }
         const int vec = forward_tile_vec(channels);
         const int64_t tiles = (channels + 8 * vec - 1) / (8 * vec);
         const int batch = forward_batch(int64_t(gx) * tiles, vec);
+        const int slot_batch = forward_slot_batch(int64_t(gx) * tiles, vec);
+        if (slot_batch > 0) {
+#define ZS_FWD_SLOT(V)                                                                         \
+    do {                                                                                         \
+        if (slot_batch == 16)                                                                    \
+            launch_slot<V, 16>(coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels,   \
+                               out, nio, gx, stream);                                            \
+        else                                                                                     \
+            launch_slot<V, 8>(coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels,    \
+                              out, nio, gx, stream);                                             \
+    } while (0)
+            switch (vec) {
+                case 1: ZS_FWD_SLOT(1); break;
+                case 2: ZS_FWD_SLOT(2); break;
+                case 3: ZS_FWD_SLOT(3); break;
+                case 4: ZS_FWD_SLOT(4); break;
+                case 5: ZS_FWD_SLOT(5); break;
+                case 6: ZS_FWD_SLOT(6); break;
+                case 7: ZS_FWD_SLOT(7); break;
+                default: ZS_FWD_SLOT(8); break;
+            }
+#undef ZS_FWD_SLOT
+            return hipGetLastError();
+        }
         switch (vec) {
             case 1: ZS_FWD_STAGED_B(1); break;
             case 2: ZS_FWD_STAGED_B(2); break;

@@ -107,8 +107,8 @@ struct NormGrad {
 
 // *deg_done (may be null) is set when grad_deg was written.
 hipError_t launch_backward(const float* grad_out, const float* coupling, const float* radial,
-                           InLayout L, const int32_t* dst32, const int32_t* rowptr,
-                           const int32_t* perm, int64_t n_nodes, int64_t n_edges,
+                           InLayout L, const int32_t* rowptr, const int32_t* perm,
+                           int64_t n_nodes, int64_t n_edges,
                            int64_t channels, float* grad_coupling, float* grad_radial, bool vec4,
                            NormGrad ng, bool* deg_done, hipStream_t stream);
 

@@ -76,7 +76,8 @@ size_t zs_csr_workspace_bytes(int64_t n_edges, int64_t n_nodes);
  *   rowptr   [n_nodes + 1] int32  rowptr[n] = #edges with dst < n (output)
  *   perm     [n_edges]     int32  perm[k] = edge at sorted position k, edges of
  *                                 equal dst in increasing edge id (output)
- *   dst32    [n_edges]     int32  int32 copy of dst, -1 where out of range (output)
+ *   dst32    [n_edges]     int32  int32 copy of dst, -1 where out of range (output;
+ *                                 zs_backward_normalized reads it)
  *   workspace, workspace_bytes >= zs_csr_workspace_bytes(n_edges, n_nodes),
  *                                 256-byte aligned device scratch
  *   bad_flag                      NULL: synchronous index check -- the call
@@ -125,7 +126,7 @@ int zs_forward(const float *coupling, const float *radial,
  *
  *   grad_out      [n_nodes][16][channels]  fp32  upstream gradient (row 0 unused)
  *   coupling, radial                       as in zs_forward
- *   dst32, rowptr, perm                    from zs_build_csr for the same dst
+ *   rowptr, perm                           from zs_build_csr for the same dst
  *   grad_coupling [n_edges][15]            fp32  fully overwritten (output)
  *   grad_radial   [n_edges][3][channels]   fp32  fully overwritten (output)
  *
@@ -137,8 +138,8 @@ int zs_forward(const float *coupling, const float *radial,
  *   where it may differ by one fp32 ulp).  Run-to-run deterministic.
  */
 int zs_backward(const float *grad_out, const float *coupling,
-                const float *radial, const int32_t *dst32,
-                const int32_t *rowptr, const int32_t *perm, int64_t n_nodes,
+                const float *radial, const int32_t *rowptr,
+                const int32_t *perm, int64_t n_nodes,
                 int64_t n_edges, int64_t channels, float *grad_coupling,
                 float *grad_radial, void *stream);
 
@@ -173,8 +174,8 @@ int zs_forward_strided(const float *coupling, int64_t coupling_edge_stride,
 int zs_backward_strided(const float *grad_out, const float *coupling,
                         int64_t coupling_edge_stride, const float *radial,
                         int64_t radial_edge_stride, int64_t radial_slot_stride,
-                        const int32_t *dst32, const int32_t *rowptr,
-                        const int32_t *perm, int64_t n_nodes, int64_t n_edges,
+                        const int32_t *rowptr, const int32_t *perm,
+                        int64_t n_nodes, int64_t n_edges,
                         int64_t channels, float *grad_coupling,
                         float *grad_radial, void *stream);
 

@@ -170,6 +170,19 @@ EDGE_CASES = [
     ("skew_small", 200, 9000, 32, "skewed_small"),
     ("nodes_20000", 20000, 40000, 8, "uniform"),      # many buckets; 4-edge forward batches
     ("nodes_3000", 3000, 90000, 32, "uniform"),       # 8-edge forward batches (2048..4095 waves)
+    # Frames with fewer wavefronts go to the slot-split forward (16-edge
+    # batches below 1280 wavefronts, 8-edge below 2048 at <= 4 channels per
+    # lane); these keep the one-wavefront-per-tile forward covered at every
+    # channel width, and the slot kernel at its 8-edge batches.
+    ("staged_c16", 2100, 40000, 16, "uniform"),
+    ("staged_c24", 2100, 40000, 24, "uniform"),
+    ("staged_c40", 1300, 40000, 40, "uniform"),
+    ("staged_c48", 1300, 40000, 48, "uniform"),
+    ("staged_c56", 1300, 40000, 56, "uniform"),
+    ("staged_c64", 1300, 40000, 64, "uniform"),
+    ("staged_c100", 1300, 30000, 100, "uniform"),     # two 64-channel tiles, the second partial
+    ("slot_b8_c32", 1500, 40000, 32, "uniform"),
+    ("slot_b8_c12", 1900, 40000, 12, "uniform"),
 ]
 
 
