@@ -557,16 +557,48 @@ void zs_bwd_staged_kernel(
         if (k0 >= k1 && !deg) continue;
         const float* gnode = grad_out + node * kRows * C;
         const float gs = ng.norm != nullptr ? ng.norm[node] : 1.0f;   // see zs_bwd_kernel
+        // Prologue in issue order: the first two steps' perm entries, then the
+        // node's upstream rows (rows 1..15 of the tile, float4 i = u*64 + lane,
+        // into registers), then the first step's operands; only then are the
+        // rows written to LDS, so the three round trips overlap (the degree
+        // gradient's out rows are read while the rows are written).  Lanes
+        // past the rows or channels load row 1's first float4 (always present)
+        // and stage zeros.
+        const bool has_edges = k0 < k1;
+        PermRaw qA{0, false}, qB{0, false};
+        if (has_edges) {
+            qA = bwd_perm_issue(perm, k0 + b, k1);
+            qB = bwd_perm_issue(perm, k0 + EPW + b, k1);
+        }
+        constexpr int kStageF4 = kZonal * T / 4;
+        constexpr int kStage = (kStageF4 + 63) / 64;
+        float4 gv[kStage];
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            const int i = u * 64 + lane;
+            const int64_t c = int64_t(i % (T / 4)) * 4;
+            const bool ok = i < kStageF4 && c < C;
+            gv[u] = *reinterpret_cast<const float4*>(
+                gnode + (ok ? int64_t(i / (T / 4) + 1) * C + c : C));
+        }
+        BwdRegs<NQ, VEC> A, B;
+        int eA = -1;
+        if (has_edges) {
+            eA = bwd_perm_resolve(qA, n_edges);
+            bwd_fetch<NQ, VEC>(A, eA, lane, cact, c0, coupling, radial, L);
+        }
         double s = 0.0;   // degree gradient: sum of grad_out * out over rows 1..15
-        for (int i = lane; i < kZonal * T / 4; i += 64) {
-            const int r = i / (T / 4) + 1;
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            const int i = u * 64 + lane;
+            if (kStageF4 % 64 != 0 && i >= kStageF4) continue;
             const int64_t c = int64_t(i % (T / 4)) * 4;
             float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             if (c < C) {
-                v = *reinterpret_cast<const float4*>(gnode + int64_t(r) * C + c);
+                v = gv[u];
                 if (deg) {
                     const float4 o = *reinterpret_cast<const float4*>(
-                        ng.out + (node * kRows + r) * C + c);
+                        ng.out + (node * kRows + i / (T / 4) + 1) * C + c);
                     s = __builtin_fma(double(v.x), double(o.x), s);
                     s = __builtin_fma(double(v.y), double(o.y), s);
                     s = __builtin_fma(double(v.z), double(o.z), s);
@@ -583,14 +615,9 @@ void zs_bwd_staged_kernel(
                 const double t = ng.norm[node];
                 ng.grad_deg[node] = t == 0.0 ? 0.0f : float(-0.5 * t * t * t * s);
             }
-            if (k0 >= k1) continue;
         }
+        if (!has_edges) continue;
         const int64_t nsteps = (k1 - k0 + EPW - 1) / EPW;
-        BwdRegs<NQ, VEC> A, B;
-        const PermRaw qA = bwd_perm_issue(perm, k0 + b, k1);
-        PermRaw qB = bwd_perm_issue(perm, k0 + EPW + b, k1);
-        int eA = bwd_perm_resolve(qA, n_edges);
-        bwd_fetch<NQ, VEC>(A, eA, lane, cact, c0, coupling, radial, L);
         for (int64_t t = 0; t < nsteps; t += 2) {
             const PermRaw qN = bwd_perm_issue(perm, k0 + (t + 2) * EPW + b, k1);
             const int eB = bwd_perm_resolve(qB, n_edges);
