@@ -40,6 +40,8 @@ class Workload:
     dst_kind: str          # "uniform" | "near_constant" | "skewed"
     envelope: bool         # coupling scaled by a per-edge cutoff-envelope factor U(0,1)
     seed: int
+    grouped: bool = False  # edges ordered by destination (as a centre-major neighbour list
+                           # gives them) instead of shuffled
 
 
 # The five workloads.  "headline" is the 4096-atom frame the pages time.
@@ -49,6 +51,10 @@ WORKLOADS = {
     "headline": Workload("headline", 4096, 647170, 32, "near_constant", True, 20261204),
     "skewed": Workload("skewed", 4096, 647170, 32, "skewed", True, 20261205),
     "large": Workload("large", 16384, 2600000, 64, "uniform", False, 20261206),
+    # the headline frame (same seed, degrees and values) with its edges grouped by
+    # destination: the CSR order is then the edge order
+    "headline_grouped": Workload("headline_grouped", 4096, 647170, 32, "near_constant", True,
+                                 20261204, grouped=True),
 }
 
 
@@ -99,11 +105,13 @@ def _skewed_degrees(n_nodes: int, n_edges: int, seed: int,
 
 
 def make_dst(w: Workload) -> np.ndarray:
-    """Destination node per edge, int64, in random edge order."""
+    """Destination node per edge, int64, in random edge order (grouped by
+    destination, in increasing node id, when ``w.grouped``)."""
     if w.n_edges == 0:
         return np.zeros(0, dtype=np.int64)
     if w.dst_kind == "uniform":
-        return _rng(w.seed, _TAG_DST).integers(0, w.n_nodes, size=w.n_edges, dtype=np.int64)
+        dst = _rng(w.seed, _TAG_DST).integers(0, w.n_nodes, size=w.n_edges, dtype=np.int64)
+        return np.sort(dst, kind="stable") if w.grouped else dst
     if w.dst_kind == "near_constant":
         deg = _near_constant_degrees(w.n_nodes, w.n_edges, w.seed)
     elif w.dst_kind == "skewed":
@@ -111,7 +119,7 @@ def make_dst(w: Workload) -> np.ndarray:
     else:
         raise ValueError(f"unknown dst_kind {w.dst_kind!r}")
     dst = np.repeat(np.arange(w.n_nodes, dtype=np.int64), deg)
-    return dst[_rng(w.seed, _TAG_SHUFFLE).permutation(w.n_edges)]
+    return dst if w.grouped else dst[_rng(w.seed, _TAG_SHUFFLE).permutation(w.n_edges)]
 
 
 def make_inputs(w: Workload | str, with_grad: bool = True, tiled_radial: bool = False) -> dict:

@@ -78,7 +78,7 @@ def compare_full(x, res, n_nodes, name):
     return check_grad_coupling(res["gc"], gc, f"{name}: grad_coupling")
 
 
-@pytest.mark.parametrize("name", ["tiny", "n1000", "headline", "skewed"])
+@pytest.mark.parametrize("name", ["tiny", "n1000", "headline", "skewed", "headline_grouped"])
 def test_workload_full(dev, name):
     w = synthetic.WORKLOADS[name]
     x = synthetic.make_inputs(w)

@@ -155,3 +155,14 @@ def test_forward_rows_of_a_node_subset_need_only_their_edges():
                                  x["dst"][edges])
     assert np.array_equal(gc_s.view(np.uint32), gc[edges].view(np.uint32))
     assert np.array_equal(gr_s.view(np.uint32), gr[edges].view(np.uint32))
+
+
+def test_grouped_headline_is_the_headline_frame_sorted():
+    """Same degrees and per-edge values as the headline frame, edges in
+    destination order (so its CSR permutation is the identity)."""
+    a = synthetic.make_inputs("headline", with_grad=False)
+    b = synthetic.make_inputs("headline_grouped", with_grad=False)
+    assert np.array_equal(np.bincount(a["dst"], minlength=4096), np.bincount(b["dst"], minlength=4096))
+    assert np.all(np.diff(b["dst"]) >= 0)
+    for k in ("coupling", "radial", "env"):
+        assert np.array_equal(a[k], b[k]), k
