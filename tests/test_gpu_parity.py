@@ -7,7 +7,7 @@ Bar (all configurations, same seeded inputs on both sides):
   * grad_coupling: |gpu - ref| <= 1e-6 + 1e-5 |ref| elementwise (the stated
     fp32 tolerance); both sides sum exact products in fp64 and round once, so
     at most a few near-ties may differ, by one fp32 ulp.
-The four smaller workloads are compared in full; the large one (E = 2.6M,
+The five smaller workloads are compared in full; the large one (E = 2.6M,
 C = 64) on sampled nodes and edges plus size-independent properties.
 """
 import sys
