@@ -394,6 +394,16 @@ __device__ __attribute__((always_inline)) inline double reduce8(double (&v)[8], 
     }
 }
 
+// grad_radial stores are non-temporal, except with 8 lanes per edge and
+// fewer than 4 channels per lane: there each store instruction writes
+// 4- or 8-byte pieces of 8 edges' rows, and plain stores, which the L2 merges
+// into whole lines, measured faster (4096-node frame, warm / caches flushed:
+// C = 24 151 -> 129 / 189 -> 158 us, C = 12 121 -> 114 / 158 -> 128 us,
+// C = 8 97 -> 98 / 129 -> 106 us); with 16 lanes per edge (C = 48) they were
+// slower (190 -> 224 us warm).
+template <int NQ, int VEC>
+constexpr bool kBwdStoreNT = ZS_BWD_NT != 0 && (NQ != 8 || VEC % 4 == 0);
+
 // gsh: the node's upstream rows 1..15, T = NQ*VEC floats each (zero past C).
 template <int NQ, int VEC, bool FULL>
 __device__ __attribute__((always_inline)) inline void bwd_compute(
@@ -454,7 +464,7 @@ __device__ __attribute__((always_inline)) inline void bwd_compute(
 #pragma unroll
             for (int s = 0; s < kSlots; ++s)
                 if (row_slot(r_lo) <= s && s <= row_slot(r_hi))
-                    store_stream_vec<VEC, ZS_BWD_NT != 0>(grow + s * C, acc[s]);
+                    store_stream_vec<VEC, kBwdStoreNT<NQ, VEC>>(grow + s * C, acc[s]);
         }
         int base;
         const double sum = reduce8<NQ>(part, q, base);
