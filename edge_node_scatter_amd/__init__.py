@@ -68,11 +68,12 @@ def load() -> ctypes.CDLL:
         lib.zs_build_csr.restype = INT
         lib.zs_forward.argtypes = [P, P, P, P, I64, I64, I64, P, P]
         lib.zs_forward.restype = INT
-        lib.zs_backward.argtypes = [P, P, P, P, P, I64, I64, I64, P, P, P]
+        lib.zs_backward.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, P, P]
         lib.zs_backward.restype = INT
         lib.zs_forward_strided.argtypes = [P, I64, P, I64, I64, P, P, I64, I64, I64, P, P]
         lib.zs_forward_strided.restype = INT
-        lib.zs_backward_strided.argtypes = [P, P, I64, P, I64, I64, P, P, I64, I64, I64, P, P, P]
+        lib.zs_backward_strided.argtypes = [P, P, I64, P, I64, I64, P, P, P, I64, I64, I64, P, P,
+                                            P]
         lib.zs_backward_strided.restype = INT
         lib.zs_forward_normalized.argtypes = [P, P, P, P, P, I64, I64, I64, P, P, P, P]
         lib.zs_forward_normalized.restype = INT
@@ -220,12 +221,12 @@ def zs_backward(grad_out: torch.Tensor, coupling: torch.Tensor, radial: torch.Te
     if grad_radial is None:
         grad_radial = torch.empty((E, SLOTS, C), dtype=torch.float32, device=radial.device)
     if coupling.is_contiguous() and radial.is_contiguous():
-        status = load().zs_backward(_ptr(grad_out), _ptr(coupling), _ptr(radial),
+        status = load().zs_backward(_ptr(grad_out), _ptr(coupling), _ptr(radial), _ptr(csr.dst32),
                                     _ptr(csr.rowptr), _ptr(csr.perm), csr.n_nodes, E, C,
                                     _ptr(grad_coupling), _ptr(grad_radial), _stream())
     else:
         status = load().zs_backward_strided(_ptr(grad_out), _ptr(coupling), cs, _ptr(radial), re,
-                                            rs, _ptr(csr.rowptr), _ptr(csr.perm),
+                                            rs, _ptr(csr.dst32), _ptr(csr.rowptr), _ptr(csr.perm),
                                             csr.n_nodes, E, C, _ptr(grad_coupling),
                                             _ptr(grad_radial), _stream())
     _check("zs_backward", status)

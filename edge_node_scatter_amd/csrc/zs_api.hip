@@ -133,16 +133,17 @@ int forward_impl(const float* coupling, int64_t cs, const float* radial, int64_t
 }
 
 int backward_impl(const float* grad_out, const float* coupling, int64_t cs, const float* radial,
-                  int64_t re, int64_t rs, const int32_t* rowptr, const int32_t* perm,
-                  int64_t n_nodes, int64_t n_edges, int64_t channels, float* grad_coupling,
-                  float* grad_radial, void* stream) {
+                  int64_t re, int64_t rs, const int32_t* dst32, const int32_t* rowptr,
+                  const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels,
+                  float* grad_coupling, float* grad_radial, void* stream) {
     if (!sizes_ok(n_edges, n_nodes) || !channels_ok(channels)) return ZS_ERR_SHAPE;
     if (!layout_ok(cs, re, rs, channels)) return ZS_ERR_SHAPE;
     if (n_edges == 0) return ZS_OK;   // both gradients are empty
-    if (!grad_out || !coupling || !radial || !rowptr || !perm || !grad_coupling || !grad_radial)
+    if (!grad_out || !coupling || !radial || !dst32 || !rowptr || !perm || !grad_coupling ||
+        !grad_radial)
         return ZS_ERR_NULL;
     if (!aligned(grad_out, 4) || !aligned(coupling, 4) || !aligned(radial, 4) ||
-        !aligned(rowptr, 4) || !aligned(perm, 4) ||
+        !aligned(dst32, 4) || !aligned(rowptr, 4) || !aligned(perm, 4) ||
         !aligned(grad_coupling, 4) || !aligned(grad_radial, 4))
         return ZS_ERR_UNSUPPORTED;
     const Range r_gc = span(grad_coupling, n_edges * zs::kZonal, 4);
@@ -150,7 +151,8 @@ int backward_impl(const float* grad_out, const float* coupling, int64_t cs, cons
     const Range ins[] = {span(grad_out, n_nodes * zs::kRows * channels, 4),
                          span(coupling, cpl_extent(n_edges, cs), 4),
                          span(radial, rad_extent(n_edges, re, rs, channels), 4),
-                         span(rowptr, n_nodes + 1, 4), span(perm, n_edges, 4)};
+                         span(dst32, n_edges, 4), span(rowptr, n_nodes + 1, 4),
+                         span(perm, n_edges, 4)};
     if (overlap(r_gc, r_gr)) return ZS_ERR_ALIAS;
     for (const Range& in : ins)
         if (overlap(r_gc, in) || overlap(r_gr, in)) return ZS_ERR_ALIAS;
@@ -181,21 +183,22 @@ int zs_forward_strided(const float* coupling, int64_t coupling_edge_stride, cons
 }
 
 int zs_backward(const float* grad_out, const float* coupling, const float* radial,
-                const int32_t* rowptr, const int32_t* perm, int64_t n_nodes, int64_t n_edges,
-                int64_t channels, float* grad_coupling, float* grad_radial, void* stream) {
+                const int32_t* dst32, const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
+                int64_t n_edges, int64_t channels, float* grad_coupling, float* grad_radial,
+                void* stream) {
     return backward_impl(grad_out, coupling, zs::kZonal, radial, zs::kSlots * channels, channels,
-                         rowptr, perm, n_nodes, n_edges, channels, grad_coupling, grad_radial,
-                         stream);
+                         dst32, rowptr, perm, n_nodes, n_edges, channels, grad_coupling,
+                         grad_radial, stream);
 }
 
 int zs_backward_strided(const float* grad_out, const float* coupling,
                         int64_t coupling_edge_stride, const float* radial,
                         int64_t radial_edge_stride, int64_t radial_slot_stride,
-                        const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
-                        int64_t n_edges, int64_t channels, float* grad_coupling,
+                        const int32_t* dst32, const int32_t* rowptr, const int32_t* perm,
+                        int64_t n_nodes, int64_t n_edges, int64_t channels, float* grad_coupling,
                         float* grad_radial, void* stream) {
     return backward_impl(grad_out, coupling, coupling_edge_stride, radial, radial_edge_stride,
-                         radial_slot_stride, rowptr, perm, n_nodes, n_edges, channels,
+                         radial_slot_stride, dst32, rowptr, perm, n_nodes, n_edges, channels,
                          grad_coupling, grad_radial, stream);
 }
 

@@ -126,7 +126,12 @@ int zs_forward(const float *coupling, const float *radial,
  *
  *   grad_out      [n_nodes][16][channels]  fp32  upstream gradient (row 0 unused)
  *   coupling, radial                       as in zs_forward
- *   rowptr, perm                           from zs_build_csr for the same dst
+ *   dst32, rowptr, perm                    from zs_build_csr for the same dst; dst32
+ *                                          is checked (non-NULL, 4-byte aligned, not
+ *                                          overlapping the outputs) but the current
+ *                                          CSR-ordered kernels do not read it: it is
+ *                                          part of the signature so that an
+ *                                          edge-ordered traversal needs no ABI change
  *   grad_coupling [n_edges][15]            fp32  fully overwritten (output)
  *   grad_radial   [n_edges][3][channels]   fp32  fully overwritten (output)
  *
@@ -138,8 +143,8 @@ int zs_forward(const float *coupling, const float *radial,
  *   where it may differ by one fp32 ulp).  Run-to-run deterministic.
  */
 int zs_backward(const float *grad_out, const float *coupling,
-                const float *radial, const int32_t *rowptr,
-                const int32_t *perm, int64_t n_nodes,
+                const float *radial, const int32_t *dst32,
+                const int32_t *rowptr, const int32_t *perm, int64_t n_nodes,
                 int64_t n_edges, int64_t channels, float *grad_coupling,
                 float *grad_radial, void *stream);
 
@@ -174,8 +179,8 @@ int zs_forward_strided(const float *coupling, int64_t coupling_edge_stride,
 int zs_backward_strided(const float *grad_out, const float *coupling,
                         int64_t coupling_edge_stride, const float *radial,
                         int64_t radial_edge_stride, int64_t radial_slot_stride,
-                        const int32_t *rowptr, const int32_t *perm,
-                        int64_t n_nodes, int64_t n_edges,
+                        const int32_t *dst32, const int32_t *rowptr,
+                        const int32_t *perm, int64_t n_nodes, int64_t n_edges,
                         int64_t channels, float *grad_coupling,
                         float *grad_radial, void *stream);
 

@@ -90,7 +90,7 @@ int main(int argc, char **argv)
     s = zs_forward(d_cpl, d_rad, d_rowptr, d_perm, N, E, C, d_out, NULL);
     if (s != ZS_OK)
         return fail_zs("zs_forward", s);
-    s = zs_backward(d_g, d_cpl, d_rad, d_rowptr, d_perm, N, E, C, d_gc, d_gr, NULL);
+    s = zs_backward(d_g, d_cpl, d_rad, d_dst32, d_rowptr, d_perm, N, E, C, d_gc, d_gr, NULL);
     if (s != ZS_OK)
         return fail_zs("zs_backward", s);
     if ((e = hipDeviceSynchronize()) != hipSuccess)

@@ -86,15 +86,16 @@ def test_forward_rejects(lib):
 
 def test_backward_rejects(lib):
     f = lib.zs_backward
-    assert f(A, B, C_, D + 4096, D + 8192, 4, 10, 0, W, X, None) == ZS_ERR_SHAPE
-    assert f(None, B, C_, D + 4096, D + 8192, 4, 10, 32, W, X, None) == ZS_ERR_NULL
-    assert f(A, B, C_, D + 4096, D + 8192, 4, 10, 32, W, None, None) == ZS_ERR_NULL
-    assert f(A, B, C_, D + 4096, D + 8192, 4, 10, 32, W + 1, X, None) == ZS_ERR_UNSUPPORTED
-    assert f(A, B, C_, D + 4096, D + 8192, 4, 10, 32, W, W + 16, None) == ZS_ERR_ALIAS
-    assert f(A, B, C_, D + 4096, D + 8192, 4, 10, 32, A, X, None) == ZS_ERR_ALIAS
-    assert f(A, B, C_, D + 4096, D + 8192, 4, 10, 32, W, C_ + 256, None) == ZS_ERR_ALIAS
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 10, 0, W, X, None) == ZS_ERR_SHAPE
+    assert f(None, B, C_, D, D + 4096, D + 8192, 4, 10, 32, W, X, None) == ZS_ERR_NULL
+    assert f(A, B, C_, None, D + 4096, D + 8192, 4, 10, 32, W, X, None) == ZS_ERR_NULL   # dst32
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 10, 32, W, None, None) == ZS_ERR_NULL
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 10, 32, W + 1, X, None) == ZS_ERR_UNSUPPORTED
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 10, 32, W, W + 16, None) == ZS_ERR_ALIAS
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 10, 32, A, X, None) == ZS_ERR_ALIAS
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 10, 32, W, C_ + 256, None) == ZS_ERR_ALIAS
     # no edges: nothing to write, returns before touching the device
-    assert f(A, B, C_, D + 4096, D + 8192, 4, 0, 32, W, X, None) == 0
+    assert f(A, B, C_, D, D + 4096, D + 8192, 4, 0, 32, W, X, None) == 0
 
 
 def test_strided_rejects(lib):
@@ -108,10 +109,10 @@ def test_strided_rejects(lib):
     assert f(A, 46, B, 160, 32, C_, D, 4, 10, 32, B + 4 * 1500, None) == ZS_ERR_ALIAS
     # out inside the strided coupling extent (9*46 + 15 floats) -> alias
     assert f(A, 46, B, 160, 32, C_, D, 4, 10, 32, A + 4 * 420, None) == ZS_ERR_ALIAS
-    assert b(A, B, -46, C_, 160, 32, D + 4096, D + 8192, 4, 10, 32, W, X, None) == ZS_ERR_SHAPE
-    assert b(A, B, 46, C_, 160, 32, D + 4096, D + 8192, 4, 10, 32, W, C_ + 4 * 1500,
+    assert b(A, B, -46, C_, 160, 32, D, D + 4096, D + 8192, 4, 10, 32, W, X, None) == ZS_ERR_SHAPE
+    assert b(A, B, 46, C_, 160, 32, D, D + 4096, D + 8192, 4, 10, 32, W, C_ + 4 * 1500,
              None) == ZS_ERR_ALIAS
-    assert b(A, B, 46, C_, 160, 32, D + 4096, D + 8192, 4, 0, 32, W, X, None) == 0
+    assert b(A, B, 46, C_, 160, 32, D, D + 4096, D + 8192, 4, 0, 32, W, X, None) == 0
 
 
 def test_normalized_rejects(lib):
