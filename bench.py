@@ -18,7 +18,12 @@ mean event-timed duration.  The headline workload is the 4096-atom frame:
 N = 4096 nodes, E = 647170 edges, C = 32 channels, fp32.
 
 The ``cpu_baseline`` leg times the CPU oracle (single-threaded plain C) on
-the same inputs.
+the same inputs.  ``copy_probe`` times a plain 256 MiB device copy in the same
+run, for context.  ``--processes N`` adds the fresh-process protocol: before
+this process touches the GPU, N child processes each run 12 warmup steps and
+50 samples of (build, forward, backward) with per-call events, with the caches
+flushed before each sample and without; ``protocol`` reports the median of the
+per-process medians.
 """
 from __future__ import annotations
 
@@ -27,6 +32,7 @@ import hashlib
 import json
 import os
 import statistics
+import subprocess
 import sys
 import time
 
@@ -244,6 +250,98 @@ def time_normalized(zs, torch, cpl, rad, x, csr, dev, steps: int) -> dict:
             "note": "bwd_us covers the scatter backward and the two degree-gradient kernels"}
 
 
+def copy_probe(torch, dev, reps: int = 10) -> dict:
+    """A plain 256 MiB device-to-device copy (torch's copy kernel), median of
+    ``reps`` event-timed copies: the bandwidth a streaming read + write reaches
+    on this GPU in the same run."""
+    n = COPY_CALIBRATION_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    us = statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3
+    moved = 2 * COPY_CALIBRATION_BYTES
+    return {"gbs": round(moved / (us * 1e-6) / 1e9, 1), "bytes_moved": moved, "us": round(us, 2),
+            "note": "torch device copy of 256 MiB (read + write), median of 10"}
+
+
+PROTOCOL_WARMUP, PROTOCOL_SAMPLES = 12, 50
+
+
+def protocol_child(zs, torch, dev, dst, cpl, rad, g, csr, ws, flag, out, gc, gr, N) -> dict:
+    """One fresh process's share of the protocol: warmup, then samples of
+    build / forward / backward with an event around each call, with the caches
+    flushed (512 MiB overwritten) before each sample and without."""
+    scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+
+    def sample(evs):
+        if evs:
+            evs[0].record()
+        zs.zs_build_csr(dst, N, workspace=ws, out=csr, bad_flag=flag)
+        if evs:
+            evs[1].record()
+        zs.zs_forward(cpl, rad, csr, out=out)
+        if evs:
+            evs[2].record()
+        zs.zs_backward(g, cpl, rad, csr, grad_coupling=gc, grad_radial=gr)
+        if evs:
+            evs[3].record()
+
+    res = {}
+    for mode in ("flushed", "warm"):
+        for _ in range(PROTOCOL_WARMUP):
+            sample(None)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+               for _ in range(PROTOCOL_SAMPLES)]
+        for i in range(PROTOCOL_SAMPLES):
+            if mode == "flushed":
+                scratch.fill_(float(i))
+            sample(evs[i])
+        torch.cuda.synchronize()
+        if int(flag.item()) != 0:
+            raise RuntimeError("destination index out of range in the synthetic input")
+
+        def med(a, b):
+            return statistics.median(e[a].elapsed_time(e[b]) for e in evs) * 1e3
+
+        res[mode] = {"build_us": med(0, 1), "fwd_us": med(1, 2), "bwd_us": med(2, 3),
+                     "fwd_bwd_us": med(1, 3)}
+    return res
+
+
+def run_protocol(args, nb) -> dict:
+    """Runs the child processes (before this process initialises the GPU) and
+    takes the median of their medians."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--protocol-child",
+           "--workload", args.workload, "--inputs", args.inputs]
+    if args.channels is not None:
+        cmd += ["--channels", str(args.channels)]
+    per = []
+    for _ in range(args.processes):
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        if r.returncode != 0:
+            raise RuntimeError(f"protocol child failed ({r.returncode}): {r.stderr[-2000:]}")
+        per.append(json.loads(r.stdout.strip().splitlines()[-1]))
+    rep = {"processes": args.processes, "warmup": PROTOCOL_WARMUP, "samples": PROTOCOL_SAMPLES}
+    for mode in ("flushed", "warm"):
+        agg = {k: round(statistics.median(p[mode][k] for p in per), 2) for k in per[0][mode]}
+        gbs = (nb["fwd"] + nb["bwd"]) / (agg["fwd_bwd_us"] * 1e-6) / 1e9
+        agg["gbs"] = round(gbs, 1)
+        agg["hbm_frac"] = round(gbs / PEAK_HBM_GBS, 4)
+        rep[mode] = agg
+    rep["per_process_fwd_bwd_us"] = {m: [round(p[m]["fwd_bwd_us"], 2) for p in per]
+                                     for m in ("flushed", "warm")}
+    rep["note"] = ("median over processes of each process's median; the fwd+bwd span has an "
+                   "event between the two calls")
+    return rep
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,6 +364,9 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 256 MiB device copy three times "
                          "(reference kernel for scaling rocprofv3 byte counters)")
+    ap.add_argument("--processes", type=int, default=0,
+                    help="also run the fresh-process protocol in this many child processes")
+    ap.add_argument("--protocol-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.write_traffic:
         print(json.dumps(write_traffic(*args.write_traffic), indent=1))
@@ -276,13 +377,17 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
-    import torch
-    import edge_node_scatter_amd as zs
-
     w = synthetic.WORKLOADS[args.workload]
     if args.channels is not None and args.channels != w.channels:
         w = synthetic.custom(f"{w.name}_c{args.channels}", w.n_nodes, w.n_edges, args.channels,
                              w.seed, w.dst_kind, w.envelope)
+    # the child processes run before this process initialises the GPU
+    protocol = (run_protocol(args, algorithmic_bytes(w.n_edges, w.n_nodes, w.channels))
+                if args.processes > 0 and not args.protocol_child else None)
+
+    import torch
+    import edge_node_scatter_amd as zs
+
     x = synthetic.make_inputs(w)
     dev = torch.device("cuda:0")
     zs.load()
@@ -323,6 +428,11 @@ def main() -> int:
         zs.zs_backward(g, cpl, rad, csr, grad_coupling=gc, grad_radial=gr)
         if evs is not None:
             evs[3].record()
+
+    if args.protocol_child:
+        print(json.dumps(protocol_child(zs, torch, dev, dst, cpl, rad, g, csr, ws, flag, out, gc,
+                                        gr, N)), flush=True)
+        return 0
 
     for _ in range(args.warmup):
         step()
@@ -404,6 +514,9 @@ def main() -> int:
         rec["flushed"] = time_flushed(zs, torch, cpl, rad, g, csr, out, gc, gr, dev, nb,
                                       min(args.steps, 20))
         rec["normalized"] = time_normalized(zs, torch, cpl, rad, x, csr, dev, args.steps)
+        rec["copy_probe"] = copy_probe(torch, dev)
+    if protocol is not None:
+        rec["protocol"] = protocol
     if args.calibrate_copy:
         src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst_copy = torch.empty_like(src)

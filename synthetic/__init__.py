@@ -51,6 +51,9 @@ WORKLOADS = {
     "headline": Workload("headline", 4096, 647170, 32, "near_constant", True, 20261204),
     "skewed": Workload("skewed", 4096, 647170, 32, "skewed", True, 20261205),
     "large": Workload("large", 16384, 2600000, 64, "uniform", False, 20261206),
+    # the headline shape with i.i.d. uniform destinations (Poisson degrees) instead
+    # of near-constant ones
+    "headline_uniform": Workload("headline_uniform", 4096, 647170, 32, "uniform", True, 20261207),
     # the headline frame (same seed, degrees and values) with its edges grouped by
     # destination: the CSR order is then the edge order
     "headline_grouped": Workload("headline_grouped", 4096, 647170, 32, "near_constant", True,

@@ -7,7 +7,7 @@ Bar (all configurations, same seeded inputs on both sides):
   * grad_coupling: |gpu - ref| <= 1e-6 + 1e-5 |ref| elementwise (the stated
     fp32 tolerance); both sides sum exact products in fp64 and round once, so
     at most a few near-ties may differ, by one fp32 ulp.
-The five smaller workloads are compared in full; the large one (E = 2.6M,
+The six smaller workloads are compared in full; the large one (E = 2.6M,
 C = 64) on sampled nodes and edges plus size-independent properties.
 """
 import sys
@@ -78,7 +78,8 @@ def compare_full(x, res, n_nodes, name):
     return check_grad_coupling(res["gc"], gc, f"{name}: grad_coupling")
 
 
-@pytest.mark.parametrize("name", ["tiny", "n1000", "headline", "skewed", "headline_grouped"])
+@pytest.mark.parametrize("name", ["tiny", "n1000", "headline", "skewed", "headline_grouped",
+                                  "headline_uniform"])
 def test_workload_full(dev, name):
     w = synthetic.WORKLOADS[name]
     x = synthetic.make_inputs(w)

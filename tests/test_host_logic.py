@@ -166,3 +166,35 @@ def test_grouped_headline_is_the_headline_frame_sorted():
     assert np.all(np.diff(b["dst"]) >= 0)
     for k in ("coupling", "radial", "env"):
         assert np.array_equal(a[k], b[k]), k
+
+
+def test_protocol_takes_the_median_of_process_medians(monkeypatch):
+    """bench.py --processes N: each child reports its medians; the parent
+    reports, per quantity, the median over the children."""
+    import argparse
+    import types
+    outs = iter([
+        {"flushed": {"build_us": 40, "fwd_us": 65, "bwd_us": 140, "fwd_bwd_us": 205},
+         "warm": {"build_us": 36, "fwd_us": 57, "bwd_us": 119, "fwd_bwd_us": 176}},
+        {"flushed": {"build_us": 42, "fwd_us": 64, "bwd_us": 150, "fwd_bwd_us": 214},
+         "warm": {"build_us": 37, "fwd_us": 58, "bwd_us": 120, "fwd_bwd_us": 178}},
+        {"flushed": {"build_us": 41, "fwd_us": 66, "bwd_us": 145, "fwd_bwd_us": 211},
+         "warm": {"build_us": 35, "fwd_us": 56, "bwd_us": 118, "fwd_bwd_us": 174}},
+    ])
+    calls = []
+
+    def fake_run(cmd, **kw):
+        calls.append(cmd)
+        return types.SimpleNamespace(returncode=0, stdout="log line\n" + json.dumps(next(outs)),
+                                     stderr="")
+
+    monkeypatch.setattr(bench.subprocess, "run", fake_run)
+    args = argparse.Namespace(processes=3, workload="headline", inputs="contiguous", channels=None)
+    nb = bench.algorithmic_bytes(647170, 4096, 32)
+    rep = bench.run_protocol(args, nb)
+    assert len(calls) == 3 and all("--protocol-child" in c for c in calls)
+    assert rep["flushed"] == {"build_us": 41, "fwd_us": 65, "bwd_us": 145, "fwd_bwd_us": 211,
+                              "gbs": round((nb["fwd"] + nb["bwd"]) / 211e-6 / 1e9, 1),
+                              "hbm_frac": round((nb["fwd"] + nb["bwd"]) / 211e-6 / 1e9 / 8000, 4)}
+    assert rep["warm"]["fwd_bwd_us"] == 176 and rep["warm"]["build_us"] == 36
+    assert rep["per_process_fwd_bwd_us"]["flushed"] == [205, 214, 211]
