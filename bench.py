@@ -529,6 +529,7 @@ def main() -> int:
             "avg_launch_us": round(bwd_us, 2),
         },
         "source_hash": {fam: kernel_source_hash(fam) for fam in KERNEL_SOURCES},
+        "input_hashes": synthetic.fingerprint(x),
     }
     if not args.no_extras:
         rec["flushed"] = time_flushed(zs, torch, cpl, rad, g, csr, out, gc, gr, dev, nb,
