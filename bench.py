@@ -173,6 +173,26 @@ def write_traffic(fetch_csv: str, write_csv: str) -> dict:
     return out
 
 
+# The GIE page's own timings of its fused Triton kernels (fp32, torch.compile
+# inference, 4096-atom diamond frame of the DPA4-Neo model, C = 32) on an
+# NVIDIA RTX 5090 (GIE page, "Numbers" section).  Another GPU and real model
+# inputs: reported beside the result for context, never as vs_baseline.
+PAGES_FWD_US, PAGES_BWD_US = 200.0, 500.0
+
+
+def pages_context(fb_us: float, nb: dict) -> dict:
+    pages_us = PAGES_FWD_US + PAGES_BWD_US
+    return {
+        "hardware": "NVIDIA RTX 5090",
+        "fwd_us": PAGES_FWD_US,
+        "bwd_us": PAGES_BWD_US,
+        "fwd_bwd_us": pages_us,
+        "algorithmic_gbs": round((nb["fwd"] + nb["bwd"]) / (pages_us * 1e-6) / 1e9, 1),
+        "time_ratio": round(pages_us / fb_us, 2),
+        "note": "the pages' fused kernels on another GPU with real model inputs; context only",
+    }
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -531,6 +551,8 @@ def main() -> int:
         "source_hash": {fam: kernel_source_hash(fam) for fam in KERNEL_SOURCES},
         "input_hashes": synthetic.fingerprint(x),
     }
+    if w.name == "headline" and args.inputs == "contiguous":
+        rec["pages_context"] = pages_context(fb_us, nb)
     if not args.no_extras:
         rec["flushed"] = time_flushed(zs, torch, cpl, rad, g, csr, out, gc, gr, dev, nb,
                                       min(args.steps, 20))

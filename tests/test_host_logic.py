@@ -198,3 +198,14 @@ def test_protocol_takes_the_median_of_process_medians(monkeypatch):
                               "hbm_frac": round((nb["fwd"] + nb["bwd"]) / 211e-6 / 1e9 / 8000, 4)}
     assert rep["warm"]["fwd_bwd_us"] == 176 and rep["warm"]["build_us"] == 36
     assert rep["per_process_fwd_bwd_us"]["flushed"] == [205, 214, 211]
+
+
+def test_pages_context_is_the_pages_timings_over_the_same_bytes():
+    """The RTX 5090 figures ride beside the result as context: 0.2 ms forward +
+    0.5 ms backward over the same algorithmic bytes (884.0 MB at the headline
+    shape) is ~1.26 TB/s, and the time ratio is 700 us over ours."""
+    nb = bench.algorithmic_bytes(647170, 4096, 32)
+    ctx = bench.pages_context(175.0, nb)
+    assert ctx["fwd_bwd_us"] == 700.0
+    assert ctx["algorithmic_gbs"] == pytest.approx(1262.9, abs=0.1)
+    assert ctx["time_ratio"] == 4.0
