@@ -116,6 +116,29 @@ def _dev_tensor(t: torch.Tensor, name: str, dtype: torch.dtype,
     return t.contiguous() if contiguous else t
 
 
+def _buffer(t: torch.Tensor, name: str, shape: tuple, dtype: torch.dtype,
+            device: torch.device) -> torch.Tensor:
+    """A caller-supplied buffer the library reads as, or writes to, a dense
+    array of ``shape``: anything else would let a kernel touch memory past it,
+    so it is rejected rather than copied."""
+    if not isinstance(t, torch.Tensor) or t.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _csr_buffers(csr: "Csr", n_edges: int, device: torch.device) -> None:
+    """The CSR arrays must hold N + 1 row offsets and E positions."""
+    _buffer(csr.rowptr, "csr.rowptr", (csr.n_nodes + 1,), torch.int32, device)
+    _buffer(csr.perm, "csr.perm", (n_edges,), torch.int32, device)
+    _buffer(csr.dst32, "csr.dst32", (n_edges,), torch.int32, device)
+
+
 def _edge_views(coupling: torch.Tensor, radial: torch.Tensor):
     """Coupling (E,15) and radial (E,3,C) as views the strided entry points
     accept (unit-stride columns / channels, non-negative strides); anything
@@ -174,9 +197,16 @@ def zs_build_csr(dst: torch.Tensor, n_nodes: int, workspace: torch.Tensor | None
         out = Csr(torch.empty(n_nodes + 1, dtype=torch.int32, device=dev),
                   torch.empty(E, dtype=torch.int32, device=dev),
                   torch.empty(E, dtype=torch.int32, device=dev), n_nodes)
+    elif out.n_nodes != n_nodes:
+        raise ValueError(f"out.n_nodes is {out.n_nodes}, expected {n_nodes}")
+    _csr_buffers(out, E, dev)
     need = zs_csr_workspace_bytes(E, n_nodes)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _buffer(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
+    if bad_flag is not None:
+        _buffer(bad_flag, "bad_flag", (1,), torch.int32, dev)
     _check("zs_build_csr", load().zs_build_csr(
         _ptr(dst), E, n_nodes, _ptr(out.rowptr), _ptr(out.perm), _ptr(out.dst32),
         _ptr(workspace), workspace.numel(), _ptr(bad_flag), _stream()))
@@ -191,8 +221,14 @@ def zs_forward(coupling: torch.Tensor, radial: torch.Tensor, csr: Csr,
     radial = _dev_tensor(radial, "radial", torch.float32, contiguous=False)
     coupling, radial, (cs, re, rs) = _edge_views(coupling, radial)
     E, C = radial.shape[0], radial.shape[2]
+    dev = radial.device
+    if coupling.device != dev:
+        raise ValueError("coupling and radial must be on the same device")
+    _csr_buffers(csr, E, dev)
     if out is None:
-        out = torch.empty((csr.n_nodes, ROWS, C), dtype=torch.float32, device=coupling.device)
+        out = torch.empty((csr.n_nodes, ROWS, C), dtype=torch.float32, device=dev)
+    else:
+        _buffer(out, "out", (csr.n_nodes, ROWS, C), torch.float32, dev)
     if coupling.is_contiguous() and radial.is_contiguous():
         status = load().zs_forward(_ptr(coupling), _ptr(radial), _ptr(csr.rowptr), _ptr(csr.perm),
                                    csr.n_nodes, E, C, _ptr(out), _stream())
@@ -214,12 +250,19 @@ def zs_backward(grad_out: torch.Tensor, coupling: torch.Tensor, radial: torch.Te
     radial = _dev_tensor(radial, "radial", torch.float32, contiguous=False)
     coupling, radial, (cs, re, rs) = _edge_views(coupling, radial)
     E, C = radial.shape[0], radial.shape[2]
-    if grad_out.shape != (csr.n_nodes, ROWS, C):
-        raise ValueError("grad_out must be (N, 16, C)")
+    dev = radial.device
+    _buffer(grad_out, "grad_out", (csr.n_nodes, ROWS, C), torch.float32, dev)
+    if coupling.device != dev:
+        raise ValueError("coupling and radial must be on the same device")
+    _csr_buffers(csr, E, dev)
     if grad_coupling is None:
-        grad_coupling = torch.empty((E, ZONAL), dtype=torch.float32, device=radial.device)
+        grad_coupling = torch.empty((E, ZONAL), dtype=torch.float32, device=dev)
+    else:
+        _buffer(grad_coupling, "grad_coupling", (E, ZONAL), torch.float32, dev)
     if grad_radial is None:
-        grad_radial = torch.empty((E, SLOTS, C), dtype=torch.float32, device=radial.device)
+        grad_radial = torch.empty((E, SLOTS, C), dtype=torch.float32, device=dev)
+    else:
+        _buffer(grad_radial, "grad_radial", (E, SLOTS, C), torch.float32, dev)
     if coupling.is_contiguous() and radial.is_contiguous():
         status = load().zs_backward(_ptr(grad_out), _ptr(coupling), _ptr(radial), _ptr(csr.dst32),
                                     _ptr(csr.rowptr), _ptr(csr.perm), csr.n_nodes, E, C,
@@ -255,6 +298,8 @@ def zs_forward_normalized(coupling: torch.Tensor, radial: torch.Tensor, env: tor
     if env.shape != (E,):
         raise ValueError("env must be (E,)")
     dev = radial.device
+    _buffer(env, "env", (E,), torch.float32, dev)
+    _csr_buffers(csr, E, dev)
     y = torch.empty((csr.n_nodes, ROWS, C), dtype=torch.float32, device=dev)
     out = torch.empty_like(y) if keep_out else None
     norm = torch.empty(csr.n_nodes, dtype=torch.float32, device=dev)
@@ -277,6 +322,10 @@ def zs_backward_normalized(grad_y: torch.Tensor, out: torch.Tensor, norm: torch.
     if grad_y.shape != (N, ROWS, C) or out.shape != (N, ROWS, C) or norm.shape != (N,):
         raise ValueError("grad_y and out must be (N, 16, C), norm (N,)")
     dev = radial.device
+    for name, t in (("grad_y", grad_y), ("out", out), ("norm", norm), ("coupling", coupling)):
+        if t.device != dev:
+            raise ValueError(f"{name} must be on {dev}")
+    _csr_buffers(csr, E, dev)
     gc = torch.empty((E, ZONAL), dtype=torch.float32, device=dev)
     gr = torch.empty((E, SLOTS, C), dtype=torch.float32, device=dev)
     ge = torch.empty(E, dtype=torch.float32, device=dev)

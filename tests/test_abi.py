@@ -190,3 +190,28 @@ def test_c_client_links_against_the_header(c_client, tmp_path):
     r = subprocess.run([c_client, str(short), str(tmp_path / "o.bin")],
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 1 and "short header" in r.stderr
+
+
+def test_binding_rejects_wrong_buffers():
+    """Caller-supplied outputs, workspace and CSR arrays must be dense arrays
+    of exactly the shape the kernels address (checked before any call)."""
+    import torch
+    cpu = torch.device("cpu")
+    ok = torch.empty((4, 16, 8))
+    assert zs._buffer(ok, "out", (4, 16, 8), torch.float32, cpu) is ok
+    with pytest.raises(ValueError, match="shape"):
+        zs._buffer(torch.empty((3, 16, 8)), "out", (4, 16, 8), torch.float32, cpu)
+    with pytest.raises(TypeError):
+        zs._buffer(torch.empty((4, 16, 8), dtype=torch.float64), "out", (4, 16, 8),
+                   torch.float32, cpu)
+    with pytest.raises(ValueError, match="contiguous"):
+        zs._buffer(torch.empty((4, 8, 16)).transpose(1, 2), "out", (4, 16, 8), torch.float32, cpu)
+    with pytest.raises(ValueError, match="tensor on"):
+        zs._buffer(ok, "out", (4, 16, 8), torch.float32, torch.device("cuda", 0))
+    csr = zs.Csr(torch.empty(5, dtype=torch.int32), torch.empty(7, dtype=torch.int32),
+                 torch.empty(7, dtype=torch.int32), 4)
+    zs._csr_buffers(csr, 7, cpu)
+    with pytest.raises(ValueError, match="csr.perm"):
+        zs._csr_buffers(csr, 8, cpu)
+    with pytest.raises(ValueError, match="csr.rowptr"):
+        zs._csr_buffers(csr._replace(n_nodes=5), 7, cpu)

@@ -224,6 +224,31 @@ def test_no_edges(dev):
     assert gc.shape == (0, 15) and gr.shape == (0, 3, C)
 
 
+def test_wrong_buffers_rejected_before_launch(dev):
+    """Output buffers and CSR arrays of the wrong size are refused by the
+    binding, and the buffers they would have overrun are left untouched."""
+    say("[gpu] wrong-sized buffers")
+    N, E, C = 9, 300, 32
+    w = synthetic.custom("wrongbuf", N, E, C, seed=5)
+    x = synthetic.make_inputs(w)
+    cpl = torch.from_numpy(x["coupling"]).to(dev)
+    rad = torch.from_numpy(x["radial"]).to(dev)
+    g = torch.from_numpy(x["grad_out"]).to(dev)
+    csr = zs.zs_build_csr(torch.from_numpy(x["dst"]).to(dev), N)
+    small = torch.full((N - 1, 16, C), float("nan"), device=dev)
+    with pytest.raises(ValueError):
+        zs.zs_forward(cpl, rad, csr, out=small)
+    with pytest.raises(ValueError):
+        zs.zs_backward(g, cpl, rad, csr, grad_radial=torch.empty((E - 1, 3, C), device=dev))
+    short = csr._replace(rowptr=csr.rowptr[:N])
+    with pytest.raises(ValueError):
+        zs.zs_forward(cpl, rad, short)
+    with pytest.raises(ValueError):
+        zs.zs_build_csr(torch.from_numpy(x["dst"]).to(dev), N, out=csr._replace(perm=csr.perm[1:]))
+    torch.cuda.synchronize()
+    assert torch.isnan(small).all()
+
+
 def test_bad_destination_rejected(dev):
     N, E = 10, 5000
     for bad in (N, -1, 1 << 40):
