@@ -173,6 +173,23 @@ def write_traffic(fetch_csv: str, write_csv: str) -> dict:
     return out
 
 
+def summarize_counters(paths: list[str]) -> dict:
+    """Mean value per dispatch of every counter, per zs:: kernel, over one or
+    more rocprofv3 --pmc counter_collection.csv files (one counter set each)."""
+    import csv
+    import collections
+
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = _kernel_short_name(r["Kernel_Name"])
+                if name.startswith("zs::"):
+                    vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: {"mean": statistics.fmean(v), "dispatches": len(v)} for c, v in sorted(cs.items())}
+            for k, cs in sorted(vals.items())}
+
+
 # The GIE page's own timings of its fused Triton kernels (fp32, torch.compile
 # inference, 4096-atom diamond frame of the DPA4-Neo model, C = 32) on an
 # NVIDIA RTX 5090 (GIE page, "Numbers" section).  Another GPU and real model
@@ -401,6 +418,9 @@ def main() -> int:
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize two rocprofv3 --pmc counter_collection.csv files "
                          "(FETCH_SIZE, WRITE_SIZE) into profiles/traffic_headline.json and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="print the mean per dispatch of every counter in these rocprofv3 --pmc "
+                         "counter_collection.csv files, per zs:: kernel, and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 256 MiB device copy three times "
                          "(reference kernel for scaling rocprofv3 byte counters)")
@@ -410,6 +430,9 @@ def main() -> int:
     args = ap.parse_args()
     if args.write_traffic:
         print(json.dumps(write_traffic(*args.write_traffic), indent=1))
+        return 0
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "

@@ -209,3 +209,22 @@ def test_pages_context_is_the_pages_timings_over_the_same_bytes():
     assert ctx["fwd_bwd_us"] == 700.0
     assert ctx["algorithmic_gbs"] == pytest.approx(1262.9, abs=0.1)
     assert ctx["time_ratio"] == 4.0
+
+
+def test_summarize_counters_means_per_kernel(tmp_path):
+    """Counter summaries average each counter over a kernel's dispatches and
+    keep only the library's kernels."""
+    rows = [("void zs::(anonymous namespace)::zs_bwd_staged_kernel<8, 4, true>(float const*)",
+             "SQ_WAVES", 16384), ("void zs::(anonymous namespace)::zs_bwd_staged_kernel<8, 4, "
+                                  "true>(float const*)", "SQ_WAVES", 16386),
+            ("at::native::fill", "SQ_WAVES", 5)]
+    p = tmp_path / "c.csv"
+    with open(p, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for k, c, v in rows:
+            wr.writerow({"Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+    got = bench.summarize_counters([str(p)])
+    assert list(got) == ["zs::zs_bwd_staged_kernel<8, 4, true>"]
+    assert got["zs::zs_bwd_staged_kernel<8, 4, true>"]["SQ_WAVES"] == {"mean": 16385.0,
+                                                                     "dispatches": 2}
