@@ -174,9 +174,14 @@ __global__ __launch_bounds__(kThreads) void csr_bucket_count_kernel(
 // Workgroup = kColBuckets buckets x kColChunks tile chunks; each thread sums
 // its chunk, the chunk sums are scanned in LDS, then the thread walks its
 // chunk again (now from the cache) rewriting it as exclusive offsets.  Block 0
-// also folds the per-tile out-of-range bits into the flag.
-constexpr int kColBuckets = 16;
+// also folds the per-tile out-of-range bits into the flag.  Up to
+// kColFewTiles tiles, 4 buckets per workgroup (four times the workgroups for
+// short columns: the 1000-node frame's whole build 25.2 vs 27.6 us, the
+// 4096-node frames' within the run-to-run spread); longer columns keep 16 (the
+// 16384-node frame's 2048 tiles: 81.6 us, against 102.9 us with 4).
 constexpr int kColChunks = 64;
+constexpr int64_t kColFewTiles = 1024;
+template <int kColBuckets>
 __global__ __launch_bounds__(kColBuckets * kColChunks) void csr_bucket_scan_kernel(
     int32_t* __restrict__ counts, int64_t tiles, int64_t n_buckets, int32_t* __restrict__ tot,
     const int32_t* __restrict__ tile_bad, int32_t* __restrict__ flag) {
@@ -538,9 +543,12 @@ hipError_t launch_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int3
                               stream>>>(dst, n_edges, n_nodes, plan.tile_edges, sb, nb, counts,
                                         tile_bad);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    csr_bucket_scan_kernel<<<grid_for(nb, kColBuckets, int64_t(1) << 30),
-                             kColBuckets * kColChunks, 0, stream>>>(counts, plan.tiles, nb, tot,
-                                                                    tile_bad, flag);
+    if (plan.tiles <= kColFewTiles)
+        csr_bucket_scan_kernel<4><<<grid_for(nb, 4, int64_t(1) << 30), 4 * kColChunks, 0,
+                                    stream>>>(counts, plan.tiles, nb, tot, tile_bad, flag);
+    else
+        csr_bucket_scan_kernel<16><<<grid_for(nb, 16, int64_t(1) << 30), 16 * kColChunks, 0,
+                                     stream>>>(counts, plan.tiles, nb, tot, tile_bad, flag);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     csr_bucket_place_kernel<<<unsigned(plan.tiles), kThreads,
                               size_t(1 + kParts) * size_t(nb) * sizeof(int32_t), stream>>>(
