@@ -224,6 +224,40 @@ def test_no_edges(dev):
     assert gc.shape == (0, 15) and gr.shape == (0, 3, C)
 
 
+def test_two_streams_at_once(dev):
+    """Two frames in flight at the same time on two streams, their launches
+    interleaved: every call works only on its own stream and buffers, so each
+    frame matches the oracle as if it ran alone."""
+    frames = [(synthetic.custom("stream_a", 300, 40000, 32, seed=71), 300),
+              (synthetic.custom("stream_b", 211, 31000, 24, seed=72), 211)]
+    say("[gpu] two streams: N=300 E=40000 C=32 and N=211 E=31000 C=24")
+    xs = [synthetic.make_inputs(w) for w, _ in frames]
+    ts = [{k: torch.from_numpy(x[k]).to(dev) for k in ("dst", "coupling", "radial", "grad_out")}
+          for x in xs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    state = [dict() for _ in frames]
+    for phase in ("build", "forward", "backward"):
+        for (w, N), s, t, st in zip(frames, streams, ts, state):
+            with torch.cuda.stream(s):
+                if phase == "build":
+                    st["flag"] = torch.zeros(1, dtype=torch.int32, device=dev)
+                    st["csr"] = zs.zs_build_csr(t["dst"], N, bad_flag=st["flag"])
+                elif phase == "forward":
+                    st["out"] = zs.zs_forward(t["coupling"], t["radial"], st["csr"])
+                else:
+                    st["gc"], st["gr"] = zs.zs_backward(t["grad_out"], t["coupling"],
+                                                        t["radial"], st["csr"])
+    torch.cuda.synchronize()
+    for (w, N), x, st in zip(frames, xs, state):
+        assert int(st["flag"].item()) == 0
+        csr = st["csr"]
+        res = {k: v.cpu().numpy() for k, v in dict(
+            rowptr=csr.rowptr, perm=csr.perm, dst32=csr.dst32, out=st["out"], gc=st["gc"],
+            gr=st["gr"]).items()}
+        compare_full(x, res, N, w.name)
+
+
 def test_wrong_buffers_rejected_before_launch(dev):
     """Output buffers and CSR arrays of the wrong size are refused by the
     binding, and the buffers they would have overrun are left untouched."""
