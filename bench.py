@@ -173,6 +173,18 @@ def write_traffic(fetch_csv: str, write_csv: str) -> dict:
     return out
 
 
+def kernel_roofline(kernel: str, alg_bytes: int, avg_us: float, headline: bool) -> dict:
+    """Algorithmic bytes per launch over the mean per-call event time, against
+    the HBM peak; ``traffic`` is the committed counter figure (HBM bytes per
+    launch) for the headline frame while the kernel's sources are unchanged."""
+    gbs = alg_bytes / (avg_us * 1e-6) / 1e9
+    traffic = load_traffic(kernel) if headline else None
+    return {"avg_launch_us": round(avg_us, 2), "algorithmic_bytes_per_launch": alg_bytes,
+            "achieved_gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "traffic_over_algorithmic": round(traffic / alg_bytes, 3) if traffic else None}
+
+
 def summarize_counters(paths: list[str]) -> dict:
     """Mean value per dispatch of every counter, per zs:: kernel, over one or
     more rocprofv3 --pmc counter_collection.csv files (one counter set each)."""
@@ -531,8 +543,8 @@ def main() -> int:
     gbs = (nb["fwd"] + nb["bwd"]) / (fb_us * 1e-6) / 1e9
     bwd_gbs = nb["bwd"] / (bwd_us * 1e-6) / 1e9
     # the committed counter summary covers the headline frame with contiguous inputs only
-    traffic = (load_traffic("zs_bwd_staged_kernel")
-               if w.name == "headline" and args.inputs == "contiguous" else None)
+    headline_frame = w.name == "headline" and args.inputs == "contiguous"
+    traffic = load_traffic("zs_bwd_staged_kernel") if headline_frame else None
 
     rec = {
         "metric": METRIC,
@@ -570,6 +582,11 @@ def main() -> int:
             "traffic": traffic,
             "algorithmic_bytes_per_launch": nb["bwd"],
             "avg_launch_us": round(bwd_us, 2),
+        },
+        "kernels": {
+            k: kernel_roofline(k, nb[part], us, headline_frame)
+            for k, part, us in (("zs_fwd_staged_kernel", "fwd", fwd_us),
+                                ("zs_bwd_staged_kernel", "bwd", bwd_us))
         },
         "source_hash": {fam: kernel_source_hash(fam) for fam in KERNEL_SOURCES},
         "input_hashes": synthetic.fingerprint(x),

@@ -228,3 +228,12 @@ def test_summarize_counters_means_per_kernel(tmp_path):
     assert list(got) == ["zs::zs_bwd_staged_kernel<8, 4, true>"]
     assert got["zs::zs_bwd_staged_kernel<8, 4, true>"]["SQ_WAVES"] == {"mean": 16385.0,
                                                                      "dispatches": 2}
+
+
+def test_kernel_roofline_figures():
+    """Per-kernel figures: algorithmic bytes over the mean launch time, as a
+    fraction of 8 TB/s; no counter figure away from the headline frame."""
+    r = bench.kernel_roofline("zs_fwd_staged_kernel", 298337156, 57.0, headline=False)
+    assert r["achieved_gbs"] == pytest.approx(5234.0, abs=0.1)
+    assert r["frac"] == pytest.approx(0.6543, abs=1e-4)
+    assert r["traffic"] is None and r["traffic_over_algorithmic"] is None
