@@ -7,8 +7,9 @@ Bar (all configurations, same seeded inputs on both sides):
   * grad_coupling: |gpu - ref| <= 1e-6 + 1e-5 |ref| elementwise (the stated
     fp32 tolerance); both sides sum exact products in fp64 and round once, so
     at most a few near-ties may differ, by one fp32 ulp.
-The six smaller workloads are compared in full; the large one (E = 2.6M,
-C = 64) on sampled nodes and edges plus size-independent properties.
+Every workload is compared in full, the large one (E = 2.6M, C = 64) too; it
+also checks the oracle's sampled entry points (used where the full oracle would
+not fit, as for offsets past 2^31) and size-independent properties.
 """
 import sys
 
@@ -89,13 +90,16 @@ def test_workload_full(dev, name):
     say(f"[gpu] workload {name}: parity ok, grad_coupling bit differences {nbits}")
 
 
-def test_workload_large_sampled(dev):
+def test_workload_large(dev):
+    """The 16384-node, C = 64 frame compared with the oracle element by element
+    (the sequential oracle takes a few seconds here), then the sampled oracle
+    entry points against the same GPU results, then properties that hold at
+    any size."""
     w = synthetic.WORKLOADS["large"]
     x = synthetic.make_inputs(w)
     say(f"[gpu] workload large: N={w.n_nodes} E={w.n_edges} C={w.channels}")
     res = run_gpu(x, dev, w.n_nodes)
-    rowptr, perm = oracle.csr(x["dst"], w.n_nodes)
-    assert np.array_equal(res["rowptr"], rowptr) and np.array_equal(res["perm"], perm)
+    compare_full(x, res, w.n_nodes, "large")
     rng = np.random.default_rng(1)
     nodes = np.concatenate([[0, w.n_nodes - 1], rng.choice(w.n_nodes, 62, replace=False)])
     ref_rows = oracle.forward_nodes(x["coupling"], x["radial"], x["dst"], w.n_nodes, nodes)
