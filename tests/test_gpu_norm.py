@@ -118,6 +118,7 @@ NORM_CASES = [
     ("c33_scalar", 8, 400, 33, "uniform"),
     ("one_edge", 5, 1, 32, "uniform"),
     ("hub", 3, 5000, 32, "uniform"),
+    ("grid_stride_c8", 1_200_000, 2_400_000, 8, "uniform"),   # more nodes than one grid holds
     ("n2500_batch8", 2500, 40000, 32, "uniform"),
     ("staged_c48", 1300, 30000, 48, "uniform"),     # one-wavefront-per-tile forward, 6 ch/lane
     ("slot_b8", 1500, 30000, 32, "uniform"),        # slot-split forward, 8-edge batches

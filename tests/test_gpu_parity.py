@@ -188,6 +188,10 @@ EDGE_CASES = [
     ("staged_c100", 1300, 30000, 100, "uniform"),     # two 64-channel tiles, the second partial
     ("slot_b8_c32", 1500, 40000, 32, "uniform"),
     ("slot_b8_c12", 1900, 40000, 12, "uniform"),
+    # More nodes than one launch's grid holds (2^20 forward workgroups, 2^20
+    # backward work items = 2^18 nodes): the kernels' grid-stride node loops.
+    ("grid_stride_c8", 1_200_000, 2_400_000, 8, "uniform"),
+    ("grid_stride_c16", 1_100_000, 1_500_000, 16, "uniform"),
 ]
 
 
