@@ -19,11 +19,18 @@ N = 4096 nodes, E = 647170 edges, C = 32 channels, fp32.
 
 The ``cpu_baseline`` leg times the CPU oracle (single-threaded plain C) on
 the same inputs.  ``copy_probe`` times a plain 256 MiB device copy in the same
-run, for context.  ``--processes N`` adds the fresh-process protocol: before
-this process touches the GPU, N child processes each run 12 warmup steps and
-50 samples of (build, forward, backward) with per-call events, with the caches
-flushed before each sample and without; ``protocol`` reports the median of the
-per-process medians.
+run, for context.  ``flushed`` times forward + backward with the caches
+emptied first by reading a 512 MiB buffer (clean lines, no write-back inside
+the sample), ``flushed_fill`` the same after overwriting it instead.
+
+The fresh-process protocol runs by default (``--processes 3``; 0 skips it):
+before this process touches the GPU, N child processes each run 12 warmup
+steps and 50 samples of (build, forward, backward) with per-call events, with
+the caches flushed before each sample (read flush, then fill flush) and
+without; ``protocol`` reports the median of the per-process medians.  Its
+``flushed`` figure is the cold-cache headline.  ``workloads`` adds the warm
+and flushed forward + backward of the 1000-node, skewed and 16384-node
+frames.
 """
 from __future__ import annotations
 
@@ -267,14 +274,45 @@ def cpu_baseline(x, w, budget_s: float = 12.0) -> dict:
     }
 
 
-def time_flushed(zs, torch, cpl, rad, g, csr, out, gc, gr, dev, nb, steps: int) -> dict:
-    """Forward + backward with the caches flushed first: a 512 MiB buffer is
-    overwritten before every sample (larger than the 256 MB memory-side cache
-    and the L2s), then forward and backward run between two events."""
-    scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+FLUSH_BYTES = 512 * 1024 * 1024   # above the 256 MB memory-side cache plus the L2s
+
+
+class Flusher:
+    """Evicts the frame from the caches before a cold sample.
+
+    ``read``: a sum over a 512 MiB buffer written once up front, so the caches
+    end up holding clean, unrelated lines and the sample pays for no
+    write-back.  ``fill``: the buffer is overwritten instead, which leaves
+    dirty lines whose write-back can fall inside the sample (kept as a second
+    figure for comparison)."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        self.acc = torch.empty((), dtype=torch.float32, device=dev)
+        self.torch = torch
+        self.i = 0
+
+    def __call__(self, mode: str) -> None:
+        if mode == "read":
+            self.torch.sum(self.buf, out=self.acc)
+        elif mode == "fill":
+            self.i += 1
+            self.buf.fill_(float(self.i))
+        else:
+            raise ValueError(mode)
+
+
+FLUSH_NOTES = {"read": "512 MiB buffer read (summed) before each sample",
+               "fill": "512 MiB buffer overwritten before each sample"}
+
+
+def time_flushed(zs, torch, flusher, mode, cpl, rad, g, csr, out, gc, gr, nb,
+                 steps: int) -> dict:
+    """Forward + backward with the caches flushed first (``Flusher``), then
+    forward and backward between two events; median over the samples."""
     ms = []
-    for i in range(steps + 2):
-        scratch.fill_(float(i))
+    for _ in range(steps + 2):
+        flusher(mode)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         zs.zs_forward(cpl, rad, csr, out=out)
@@ -287,7 +325,7 @@ def time_flushed(zs, torch, cpl, rad, g, csr, out, gc, gr, dev, nb, steps: int) 
     gbs = (nb["fwd"] + nb["bwd"]) / (med * 1e-6) / 1e9
     return {"fwd_bwd_us_median": round(med, 2), "gbs": round(gbs, 1),
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "samples": len(t),
-            "note": "512 MiB buffer overwritten before each sample"}
+            "note": FLUSH_NOTES[mode]}
 
 
 def time_normalized(zs, torch, cpl, rad, x, csr, dev, steps: int) -> dict:
@@ -340,14 +378,77 @@ def copy_probe(torch, dev, reps: int = 10) -> dict:
             "note": "torch device copy of 256 MiB (read + write), median of 10"}
 
 
+WORKLOADS_REPORTED = ("n1000", "skewed", "large")
+
+
+def time_workloads(zs, torch, dev, names, steps: int) -> dict:
+    """Warm and cache-flushed forward + backward of other frames, in this
+    process after the headline's timed region: per frame, the CSR build once,
+    a few warmup passes, then ``steps`` back-to-back passes with an event
+    around each call (warm) and ``min(steps, 20)`` samples each preceded by
+    the read flush (flushed).  Inputs are freed before the next frame."""
+    rep = {}
+    for name in names:
+        w = synthetic.WORKLOADS[name]
+        x = synthetic.make_inputs(w)
+        E, N, C = w.n_edges, w.n_nodes, w.channels
+        t = {k: torch.from_numpy(x[k]).to(dev) for k in ("dst", "coupling", "radial", "grad_out")}
+        del x
+        csr = zs.zs_build_csr(t["dst"], N)
+        out = torch.empty((N, 16, C), device=dev)
+        gc = torch.empty((E, 15), device=dev)
+        gr = torch.empty((E, 3, C), device=dev)
+        flusher = Flusher(torch, dev)
+        nb = algorithmic_bytes(E, N, C)
+
+        def pair(evs):
+            evs[0].record()
+            zs.zs_forward(t["coupling"], t["radial"], csr, out=out)
+            evs[1].record()
+            zs.zs_backward(t["grad_out"], t["coupling"], t["radial"], csr, grad_coupling=gc,
+                           grad_radial=gr)
+            evs[2].record()
+
+        res = {}
+        for mode, n in (("warm", steps), ("flushed", min(steps, 20))):
+            for _ in range(3):
+                pair([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+            for e in evs:
+                if mode == "flushed":
+                    flusher("read")
+                pair(e)
+            torch.cuda.synchronize()
+            fwd = statistics.median(e[0].elapsed_time(e[1]) for e in evs) * 1e3
+            bwd = statistics.median(e[1].elapsed_time(e[2]) for e in evs) * 1e3
+            fb = statistics.median(e[0].elapsed_time(e[2]) for e in evs) * 1e3
+            gbs = (nb["fwd"] + nb["bwd"]) / (fb * 1e-6) / 1e9
+            res[mode] = {"fwd_us": round(fwd, 2), "bwd_us": round(bwd, 2),
+                         "fwd_bwd_us": round(fb, 2), "gbs": round(gbs, 1),
+                         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        rep[name] = {"n_nodes": N, "n_edges": E, "channels": C,
+                     "algorithmic_bytes": nb["fwd"] + nb["bwd"],
+                     "target_us_at_60pct": round((nb["fwd"] + nb["bwd"]) /
+                                                 (0.6 * PEAK_HBM_GBS * 1e9) * 1e6, 1),
+                     **res}
+        del t, csr, out, gc, gr, flusher
+        torch.cuda.empty_cache()
+    rep["note"] = ("medians per call, forward and backward with an event between them; flushed: "
+                   + FLUSH_NOTES["read"])
+    return rep
+
+
 PROTOCOL_WARMUP, PROTOCOL_SAMPLES = 12, 50
+
+
+PROTOCOL_MODES = {"flushed": "read", "flushed_fill": "fill", "warm": None}
 
 
 def protocol_child(zs, torch, dev, dst, cpl, rad, g, csr, ws, flag, out, gc, gr, N) -> dict:
     """One fresh process's share of the protocol: warmup, then samples of
     build / forward / backward with an event around each call, with the caches
-    flushed (512 MiB overwritten) before each sample and without."""
-    scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    flushed before each sample (read flush, then fill flush) and without."""
+    flusher = Flusher(torch, dev)
 
     def sample(evs):
         if evs:
@@ -363,14 +464,14 @@ def protocol_child(zs, torch, dev, dst, cpl, rad, g, csr, ws, flag, out, gc, gr,
             evs[3].record()
 
     res = {}
-    for mode in ("flushed", "warm"):
+    for mode, flush in PROTOCOL_MODES.items():
         for _ in range(PROTOCOL_WARMUP):
             sample(None)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
                for _ in range(PROTOCOL_SAMPLES)]
         for i in range(PROTOCOL_SAMPLES):
-            if mode == "flushed":
-                scratch.fill_(float(i))
+            if flush is not None:
+                flusher(flush)
             sample(evs[i])
         torch.cuda.synchronize()
         if int(flag.item()) != 0:
@@ -398,16 +499,17 @@ def run_protocol(args, nb) -> dict:
             raise RuntimeError(f"protocol child failed ({r.returncode}): {r.stderr[-2000:]}")
         per.append(json.loads(r.stdout.strip().splitlines()[-1]))
     rep = {"processes": args.processes, "warmup": PROTOCOL_WARMUP, "samples": PROTOCOL_SAMPLES}
-    for mode in ("flushed", "warm"):
+    for mode in PROTOCOL_MODES:
         agg = {k: round(statistics.median(p[mode][k] for p in per), 2) for k in per[0][mode]}
         gbs = (nb["fwd"] + nb["bwd"]) / (agg["fwd_bwd_us"] * 1e-6) / 1e9
         agg["gbs"] = round(gbs, 1)
         agg["hbm_frac"] = round(gbs / PEAK_HBM_GBS, 4)
         rep[mode] = agg
     rep["per_process_fwd_bwd_us"] = {m: [round(p[m]["fwd_bwd_us"], 2) for p in per]
-                                     for m in ("flushed", "warm")}
+                                     for m in PROTOCOL_MODES}
     rep["note"] = ("median over processes of each process's median; the fwd+bwd span has an "
-                   "event between the two calls")
+                   "event between the two calls; flushed: " + FLUSH_NOTES["read"] +
+                   "; flushed_fill: " + FLUSH_NOTES["fill"])
     return rep
 
 
@@ -436,8 +538,11 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 256 MiB device copy three times "
                          "(reference kernel for scaling rocprofv3 byte counters)")
-    ap.add_argument("--processes", type=int, default=0,
-                    help="also run the fresh-process protocol in this many child processes")
+    ap.add_argument("--processes", type=int, default=3,
+                    help="fresh-process protocol in this many child processes (0: skip it)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the warm and cache-flushed timings of the other frames "
+                         "(1000-node, skewed, 16384-node) that the headline run reports")
     ap.add_argument("--protocol-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.write_traffic:
@@ -594,12 +699,21 @@ def main() -> int:
     if w.name == "headline" and args.inputs == "contiguous":
         rec["pages_context"] = pages_context(fb_us, nb)
     if not args.no_extras:
-        rec["flushed"] = time_flushed(zs, torch, cpl, rad, g, csr, out, gc, gr, dev, nb,
-                                      min(args.steps, 20))
+        flusher = Flusher(torch, dev)
+        n_flushed = min(args.steps, 20)
+        rec["flushed"] = time_flushed(zs, torch, flusher, "read", cpl, rad, g, csr, out, gc, gr,
+                                      nb, n_flushed)
+        rec["flushed_fill"] = time_flushed(zs, torch, flusher, "fill", cpl, rad, g, csr, out, gc,
+                                           gr, nb, n_flushed)
+        del flusher
         rec["normalized"] = time_normalized(zs, torch, cpl, rad, x, csr, dev, args.steps)
         rec["copy_probe"] = copy_probe(torch, dev)
     if protocol is not None:
         rec["protocol"] = protocol
+    if (w.name == "headline" and args.inputs == "contiguous" and args.channels is None
+            and not args.no_workloads and not args.no_extras):
+        del out, gc, gr, ws
+        rec["workloads"] = time_workloads(zs, torch, dev, WORKLOADS_REPORTED, args.steps)
     if args.calibrate_copy:
         src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst_copy = torch.empty_like(src)

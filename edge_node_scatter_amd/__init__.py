@@ -369,12 +369,11 @@ class _GieZonalScatterNormalized(torch.autograd.Function):
         y, out, norm = zs_forward_normalized(coupling, radial, env, csr)
         ctx.save_for_backward(coupling, radial, out, norm, rowptr, perm, dst32)
         ctx.n_nodes = n_nodes
-        ctx.mark_non_differentiable(norm)
-        return y, norm
+        return y
 
     @staticmethod
     @torch.autograd.function.once_differentiable
-    def backward(ctx, grad_y, grad_norm):
+    def backward(ctx, grad_y):
         coupling, radial, out, norm, rowptr, perm, dst32 = ctx.saved_tensors
         csr = Csr(rowptr, perm, dst32, ctx.n_nodes)
         if grad_y is None:
@@ -385,10 +384,12 @@ class _GieZonalScatterNormalized(torch.autograd.Function):
 
 
 def gie_zonal_scatter_normalized(coupling: torch.Tensor, radial: torch.Tensor, env: torch.Tensor,
-                                 csr: Csr) -> tuple[torch.Tensor, torch.Tensor]:
+                                 csr: Csr) -> torch.Tensor:
     """Differentiable scatter followed by the degree normalisation:
-    returns (y, norm), y = scatter * norm[:, None, None], norm = deg^(-1/2)
-    with deg the per-node sum of ``env``.  Gradients flow to coupling, radial
-    and env (norm itself is returned as a non-differentiable by-product)."""
+    returns y = scatter * norm[:, None, None], norm = deg^(-1/2) with deg the
+    per-node sum of ``env``.  Gradients flow to coupling, radial and env.
+    The per-node factor itself is not returned here (a caller that used it
+    downstream would expect a gradient through it, which this function does
+    not carry); ``zs_forward_normalized`` returns it as a plain tensor."""
     return _GieZonalScatterNormalized.apply(coupling, radial, env, csr.rowptr, csr.perm,
                                             csr.dst32, csr.n_nodes)

@@ -413,11 +413,13 @@ __device__ __attribute__((always_inline)) inline void bwd_compute(
     constexpr int EPW = BwdRegs<NQ, VEC>::EPW;
     constexpr int T = NQ * VEC;
     // stage this step's coupling rows, then read the 15 weights of edge slot b
+    wave_lds_sync();   // the previous step's reads come before these writes
 #pragma unroll
     for (int i = 0; i < BwdRegs<NQ, VEC>::CPL; ++i) {
         const int idx = i * 64 + lane;
         if (idx < EPW * kZonal) wsh[(idx / kZonal) * 16 + idx % kZonal] = R.w[i];
     }
+    wave_lds_sync();   // each lane reads the rows other lanes staged
     float w[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -598,6 +600,7 @@ void zs_bwd_staged_kernel(
             bwd_fetch<NQ, VEC>(A, eA, lane, cact, c0, coupling, radial, L);
         }
         double s = 0.0;   // degree gradient: sum of grad_out * out over rows 1..15
+        wave_lds_sync();   // the previous item's reads of the rows come before these writes
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
             const int i = u * 64 + lane;
@@ -618,6 +621,7 @@ void zs_bwd_staged_kernel(
             }
             gsh4[i] = v;
         }
+        wave_lds_sync();   // every lane reads rows other lanes staged
         if (deg) {
 #pragma unroll
             for (int h = 32; h >= 1; h >>= 1) s = s + __shfl_xor(s, h, 64);

@@ -328,6 +328,7 @@ __global__ __launch_bounds__(kThreads) void csr_bucket_place_kernel(
             const int cnt = __popcll(same);
             const int leader = ok ? __ffsll((unsigned long long)same) - 1 : lane;
             int32_t o = 0;
+            wave_lds_sync();   // the previous step's leaders wrote run[] entries read here
             if (ok && rank == 0) {
                 o = run[bucket];
                 run[bucket] = o + cnt;
@@ -459,6 +460,7 @@ __global__ __launch_bounds__(kThreads) void csr_node_place_kernel(
             const int cnt = __popcll(same);
             const int leader = ok ? __ffsll((unsigned long long)same) - 1 : lane;
             int32_t o = 0;
+            if (kLds) wave_lds_sync();   // the previous step's leaders wrote run[] entries read here
             if (ok && rank == 0) {
                 if (kLds) {
                     o = run[loc];

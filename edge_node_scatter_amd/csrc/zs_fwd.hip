@@ -1,10 +1,12 @@
 // Fused GIE zonal scatter, forward, gfx950.
 //
-// deepmd-kit PR #6072 ("fused Triton zonal scatter for the GIE head"), section
-// "What", Forward bullet: a node-parallel kernel walks the stable destination
-// CSR, keeps the node's message sum in registers and writes the padded
-// (N, 16, C) layout with a zero scalar row; the (E, 15, C) message surface is
-// never formed.
+// Operation: deepmd-kit PR #6072 ("fused Triton zonal scatter for the GIE
+// head"), section "What", Forward bullet.  Each node's output rows are summed
+// by the wavefront that owns the node: it visits the node's incoming edges in
+// destination-sorted order, multiplies each edge's coupling weight into its
+// radial features on the fly and adds the product into registers.  Per-edge
+// products therefore never exist in memory; the only write is the node's
+// 16-row block, whose row 0 is stored as zeros.
 //
 // Three kernels, chosen per launch: zs_fwd_staged_kernel (one wavefront per
 // node and channel tile, C % 4 == 0, aligned), zs_fwd_slot_kernel (three
@@ -289,6 +291,7 @@ __device__ __attribute__((always_inline)) inline void fwd_stage_accumulate(
     const FwdRegs<VEC, B>& R, float4* rsh, float* csh, int cnt, int lane, int q, int j, int sA,
     int sB, float (&acc0)[VEC], float (&acc1)[VEC], float& deg) {
     using S = FwdShape<VEC, B>;
+    wave_lds_sync();   // the previous batch's reads come before these writes
 #pragma unroll
     for (int i = 0; i < S::RV; ++i)
         if (S::RAD % 64 == 0 || i * 64 + lane < S::RAD) rsh[i * 64 + lane] = R.r[i];
@@ -300,6 +303,7 @@ __device__ __attribute__((always_inline)) inline void fwd_stage_accumulate(
         else if (NORM && idx < B * (kZonal + 1))
             csh[(idx - B * kZonal) * 16 + 15] = R.w[i];
     }
+    wave_lds_sync();   // every lane reads values other lanes staged
     const float* rf = reinterpret_cast<const float*>(rsh);
     auto edge = [&](int b) {
         if (NORM) deg = deg + csh[b * 16 + 15];
@@ -517,12 +521,14 @@ __global__ __launch_bounds__(192) void zs_fwd_slot_kernel(const float* __restric
         };
         auto stage_accumulate = [&](const float4 (&rr)[S::RV], const float (&ww)[S::CV],
                                     int cnt) {
+            wave_lds_sync();   // the previous batch's reads come before these writes
 #pragma unroll
             for (int i = 0; i < S::RV; ++i)
                 if (S::RAD % 64 == 0 || i * 64 + lane < S::RAD) rsh[i * 64 + lane] = rr[i];
 #pragma unroll
             for (int i = 0; i < S::CV; ++i)
                 if (S::CW % 64 == 0 || i * 64 + lane < S::CW) csh[i * 64 + lane] = ww[i];
+            wave_lds_sync();   // every lane reads values other lanes staged
             const float* rf = reinterpret_cast<const float*>(rsh);
             const int jw = j < nr ? j : 0;
             auto edge = [&](int b) {

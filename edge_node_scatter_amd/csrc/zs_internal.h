@@ -16,6 +16,20 @@ constexpr int kRows = 16;
 constexpr int kZonal = 15;
 constexpr int kSlots = 3;
 
+// Orders LDS accesses between the lanes of one wavefront.  A lane that reads
+// what another lane of its wavefront wrote to LDS, or overwrites what another
+// lane still has to read, relies on the accesses on either side of this
+// point staying on their side: the release fence keeps earlier accesses
+// before it, the acquire fence keeps later ones after it, and the wave
+// barrier keeps the two fences together.  At wavefront scope none of the
+// three emits an instruction (a wavefront's LDS operations complete in issue
+// order); they only bind the compiler.
+__device__ __attribute__((always_inline)) inline void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Vector of VEC consecutive fp32 channels (VEC = 4: one 16-byte access).
 template <int VEC>
 struct VecT;

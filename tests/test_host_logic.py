@@ -175,10 +175,13 @@ def test_protocol_takes_the_median_of_process_medians(monkeypatch):
     import types
     outs = iter([
         {"flushed": {"build_us": 40, "fwd_us": 65, "bwd_us": 140, "fwd_bwd_us": 205},
+         "flushed_fill": {"build_us": 40, "fwd_us": 66, "bwd_us": 141, "fwd_bwd_us": 207},
          "warm": {"build_us": 36, "fwd_us": 57, "bwd_us": 119, "fwd_bwd_us": 176}},
         {"flushed": {"build_us": 42, "fwd_us": 64, "bwd_us": 150, "fwd_bwd_us": 214},
+         "flushed_fill": {"build_us": 42, "fwd_us": 65, "bwd_us": 151, "fwd_bwd_us": 216},
          "warm": {"build_us": 37, "fwd_us": 58, "bwd_us": 120, "fwd_bwd_us": 178}},
         {"flushed": {"build_us": 41, "fwd_us": 66, "bwd_us": 145, "fwd_bwd_us": 211},
+         "flushed_fill": {"build_us": 41, "fwd_us": 67, "bwd_us": 146, "fwd_bwd_us": 213},
          "warm": {"build_us": 35, "fwd_us": 56, "bwd_us": 118, "fwd_bwd_us": 174}},
     ])
     calls = []
@@ -198,6 +201,7 @@ def test_protocol_takes_the_median_of_process_medians(monkeypatch):
                               "hbm_frac": round((nb["fwd"] + nb["bwd"]) / 211e-6 / 1e9 / 8000, 4)}
     assert rep["warm"]["fwd_bwd_us"] == 176 and rep["warm"]["build_us"] == 36
     assert rep["per_process_fwd_bwd_us"]["flushed"] == [205, 214, 211]
+    assert rep["flushed_fill"]["fwd_bwd_us"] == 213
 
 
 def test_pages_context_is_the_pages_timings_over_the_same_bytes():
