@@ -294,7 +294,7 @@ class Flusher:
 
     def __call__(self, mode: str) -> None:
         if mode == "read":
-            self.torch.sum(self.buf, out=self.acc)
+            self.torch.sum(self.buf, dim=0, out=self.acc)
         elif mode == "fill":
             self.i += 1
             self.buf.fill_(float(self.i))
@@ -381,6 +381,11 @@ def copy_probe(torch, dev, reps: int = 10) -> dict:
 WORKLOADS_REPORTED = ("n1000", "skewed", "large")
 
 
+def progress(msg: str) -> None:
+    """A progress line on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def time_workloads(zs, torch, dev, names, steps: int) -> dict:
     """Warm and cache-flushed forward + backward of other frames, in this
     process after the headline's timed region: per frame, the CSR build once,
@@ -433,6 +438,8 @@ def time_workloads(zs, torch, dev, names, steps: int) -> dict:
                      **res}
         del t, csr, out, gc, gr, flusher
         torch.cuda.empty_cache()
+        progress(f"workload {name}: warm {res['warm']['fwd_bwd_us']} us, "
+                 f"flushed {res['flushed']['fwd_bwd_us']} us")
     rep["note"] = ("medians per call, forward and backward with an event between them; flushed: "
                    + FLUSH_NOTES["read"])
     return rep
@@ -498,6 +505,8 @@ def run_protocol(args, nb) -> dict:
         if r.returncode != 0:
             raise RuntimeError(f"protocol child failed ({r.returncode}): {r.stderr[-2000:]}")
         per.append(json.loads(r.stdout.strip().splitlines()[-1]))
+        progress(f"protocol child {len(per)}/{args.processes}: flushed "
+                 f"{per[-1]['flushed']['fwd_bwd_us']:.1f} us, warm {per[-1]['warm']['fwd_bwd_us']:.1f} us")
     rep = {"processes": args.processes, "warmup": PROTOCOL_WARMUP, "samples": PROTOCOL_SAMPLES}
     for mode in PROTOCOL_MODES:
         agg = {k: round(statistics.median(p[mode][k] for p in per), 2) for k in per[0][mode]}
@@ -627,6 +636,7 @@ def main() -> int:
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    progress(f"timed steps done: {args.steps} steps in {wall:.3f} s")
     if int(flag.item()) != 0:
         raise RuntimeError("destination index out of range in the synthetic input")
 
@@ -722,6 +732,7 @@ def main() -> int:
         torch.cuda.synchronize()
         rec["copy_calibration_bytes"] = COPY_CALIBRATION_BYTES
     if not args.no_cpu_baseline:
+        progress("timing the CPU oracle")
         rec["cpu_baseline"] = cpu_baseline(x, w)
     print(json.dumps(rec), flush=True)
     return 0
