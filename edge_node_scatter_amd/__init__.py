@@ -66,6 +66,8 @@ def load() -> ctypes.CDLL:
         lib.zs_csr_workspace_bytes.restype = SZ
         lib.zs_build_csr.argtypes = [P, I64, I64, P, P, P, P, SZ, P, P]
         lib.zs_build_csr.restype = INT
+        lib.zs_build_csr_noalloc.argtypes = [P, I64, I64, P, P, P, P, P]
+        lib.zs_build_csr_noalloc.restype = INT
         lib.zs_forward.argtypes = [P, P, P, P, I64, I64, I64, P, P]
         lib.zs_forward.restype = INT
         lib.zs_backward.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, P, P]
@@ -210,6 +212,31 @@ def zs_build_csr(dst: torch.Tensor, n_nodes: int, workspace: torch.Tensor | None
     _check("zs_build_csr", load().zs_build_csr(
         _ptr(dst), E, n_nodes, _ptr(out.rowptr), _ptr(out.perm), _ptr(out.dst32),
         _ptr(workspace), workspace.numel(), _ptr(bad_flag), _stream()))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def zs_build_csr_noalloc(dst: torch.Tensor, n_nodes: int, out: Csr,
+                         bad_flag: torch.Tensor | None = None) -> Csr:
+    """zs_build_csr with the library's fixed per-device scratch instead of a
+    workspace: the call allocates nothing, so the output arrays must be
+    passed in (``out``).  Raises ZsError (ZS_ERR_SCRATCH) when the sizes need
+    more than NOALLOC_SCRATCH_BYTES of scratch.  Calls that overlap on one
+    device share that scratch and must not run concurrently."""
+    dst = _dev_tensor(dst, "dst", torch.int64, contiguous=False)
+    if not dst.is_contiguous():
+        raise ValueError("dst must be contiguous")
+    E = dst.numel()
+    if out.n_nodes != n_nodes:
+        raise ValueError(f"out.n_nodes is {out.n_nodes}, expected {n_nodes}")
+    _csr_buffers(out, E, dst.device)
+    if bad_flag is not None:
+        _buffer(bad_flag, "bad_flag", (1,), torch.int32, dst.device)
+    _check("zs_build_csr_noalloc", load().zs_build_csr_noalloc(
+        _ptr(dst), E, n_nodes, _ptr(out.rowptr), _ptr(out.perm), _ptr(out.dst32),
+        _ptr(bad_flag), _stream()))
     return out
 
 

@@ -3,10 +3,36 @@
 // call leaves device state untouched.
 #include "zs.h"
 
+#include <mutex>
+
 #include "zs_csr.h"
 #include "zs_internal.h"
 
 namespace {
+
+// Scratch of zs_build_csr_noalloc: one copy per device, created with the code
+// object.  Host code never uses this name as an address (on the host it is a
+// stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[ZS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // guarded by g_scratch_mutex
+
+// Device address of the current device's scratch; NULL if HIP fails.
+void* noalloc_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
 
 struct Range {
     uintptr_t lo, hi;   // [lo, hi)
@@ -43,6 +69,8 @@ const char* zs_status_string(int status) {
         case ZS_ERR_ALIAS: return "an output overlaps an input or another output";
         case ZS_ERR_WORKSPACE: return "workspace is NULL or too small";
         case ZS_ERR_HIP: return "a HIP runtime call failed";
+        case ZS_ERR_SCRATCH:
+            return "the sizes need more scratch than the library's fixed device buffer holds";
         default: return "unknown status";
     }
 }
@@ -52,9 +80,13 @@ size_t zs_csr_workspace_bytes(int64_t n_edges, int64_t n_nodes) {
     return zs::plan_csr(n_edges, n_nodes).bytes;
 }
 
-int zs_build_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* rowptr,
-                 int32_t* perm, int32_t* dst32, void* workspace, size_t workspace_bytes,
-                 int32_t* bad_flag, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of the CSR build's buffers (not the workspace).
+int csr_args(const int64_t* dst, int64_t n_edges, int64_t n_nodes, const int32_t* rowptr,
+             const int32_t* perm, const int32_t* dst32, const int32_t* bad_flag) {
     if (!sizes_ok(n_edges, n_nodes)) return ZS_ERR_SHAPE;
     if (!rowptr || (n_edges > 0 && (!dst || !perm || !dst32))) return ZS_ERR_NULL;
     if (!aligned(rowptr, 4) || (n_edges > 0 && (!aligned(dst, 8) || !aligned(perm, 4) ||
@@ -69,19 +101,20 @@ int zs_build_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* 
         overlap(r_flag, r_dst) || overlap(r_flag, r_rowptr) || overlap(r_flag, r_perm) ||
         overlap(r_flag, r_dst32))
         return ZS_ERR_ALIAS;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    return ZS_OK;
+}
+
+// The build on checked arguments.  With n_edges > 0 the workspace holds at
+// least plan.bytes and overlaps none of the buffers.
+int csr_run(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* rowptr,
+            int32_t* perm, int32_t* dst32, void* workspace, int32_t* bad_flag,
+            hipStream_t s) {
     if (n_edges == 0) {
         hipError_t err = zs::launch_fill_i32(rowptr, n_nodes + 1, 0, s);
         if (err == hipSuccess && bad_flag) err = zs::launch_fill_i32(bad_flag, 1, 0, s);
         return hip_status(err);
     }
     const zs::CsrPlan plan = zs::plan_csr(n_edges, n_nodes);
-    if (!workspace || workspace_bytes < plan.bytes) return ZS_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return ZS_ERR_UNSUPPORTED;
-    const Range r_ws = span(workspace, int64_t(plan.bytes), 1);
-    if (overlap(r_ws, r_dst) || overlap(r_ws, r_rowptr) || overlap(r_ws, r_perm) ||
-        overlap(r_ws, r_dst32) || overlap(r_ws, r_flag))
-        return ZS_ERR_ALIAS;
     hipError_t err = zs::launch_csr(dst, n_edges, n_nodes, rowptr, perm, dst32, workspace, plan,
                                     bad_flag, s);
     if (err != hipSuccess) return ZS_ERR_HIP;
@@ -94,6 +127,47 @@ int zs_build_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* 
     if (hipStreamSynchronize(s) != hipSuccess) return ZS_ERR_HIP;
     return flag ? ZS_ERR_INDEX : ZS_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+int zs_build_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* rowptr,
+                 int32_t* perm, int32_t* dst32, void* workspace, size_t workspace_bytes,
+                 int32_t* bad_flag, void* stream) {
+    const int st = csr_args(dst, n_edges, n_nodes, rowptr, perm, dst32, bad_flag);
+    if (st != ZS_OK) return st;
+    if (n_edges > 0) {
+        const zs::CsrPlan plan = zs::plan_csr(n_edges, n_nodes);
+        if (!workspace || workspace_bytes < plan.bytes) return ZS_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return ZS_ERR_UNSUPPORTED;
+        const Range r_ws = span(workspace, int64_t(plan.bytes), 1);
+        if (overlap(r_ws, span(dst, n_edges, 8)) || overlap(r_ws, span(rowptr, n_nodes + 1, 4)) ||
+            overlap(r_ws, span(perm, n_edges, 4)) || overlap(r_ws, span(dst32, n_edges, 4)) ||
+            overlap(r_ws, span(bad_flag, bad_flag ? 1 : 0, 4)))
+            return ZS_ERR_ALIAS;
+    }
+    return csr_run(dst, n_edges, n_nodes, rowptr, perm, dst32, workspace, bad_flag,
+                   static_cast<hipStream_t>(stream));
+}
+
+int zs_build_csr_noalloc(const int64_t* dst, int64_t n_edges, int64_t n_nodes,
+                         int32_t* rowptr, int32_t* perm, int32_t* dst32, int32_t* bad_flag,
+                         void* stream) {
+    const int st = csr_args(dst, n_edges, n_nodes, rowptr, perm, dst32, bad_flag);
+    if (st != ZS_OK) return st;
+    void* ws = nullptr;
+    if (n_edges > 0) {
+        if (zs::plan_csr(n_edges, n_nodes).bytes > size_t(ZS_NOALLOC_SCRATCH_BYTES))
+            return ZS_ERR_SCRATCH;
+        ws = noalloc_scratch();   // first call on this device: symbol lookup, no allocation
+        if (ws == nullptr) return ZS_ERR_HIP;
+    }
+    return csr_run(dst, n_edges, n_nodes, rowptr, perm, dst32, ws, bad_flag,
+                   static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
 
 namespace {
 
@@ -166,6 +240,8 @@ int backward_impl(const float* grad_out, const float* coupling, int64_t cs, cons
 }
 
 }  // namespace
+
+extern "C" {
 
 int zs_forward(const float* coupling, const float* radial, const int32_t* rowptr,
                const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels, float* out,

@@ -56,7 +56,9 @@ typedef enum zs_status {
     ZS_ERR_UNSUPPORTED = -4, /* an fp32/int32 pointer is not 4-byte aligned     */
     ZS_ERR_ALIAS = -5,       /* an output overlaps an input or another output   */
     ZS_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required         */
-    ZS_ERR_HIP = -7          /* a HIP runtime call (launch, copy, sync) failed  */
+    ZS_ERR_HIP = -7,         /* a HIP runtime call (launch, copy, sync) failed  */
+    ZS_ERR_SCRATCH = -8      /* the sizes need more scratch than the library's
+                                fixed device buffer holds (zs_build_csr_noalloc) */
 } zs_status;
 
 /* Static, human-readable text for a status code; never NULL. */
@@ -96,6 +98,33 @@ int zs_build_csr(const int64_t *dst, int64_t n_edges, int64_t n_nodes,
                  int32_t *rowptr, int32_t *perm, int32_t *dst32,
                  void *workspace, size_t workspace_bytes, int32_t *bad_flag,
                  void *stream);
+
+/*
+ * zs_build_csr_noalloc -- zs_build_csr for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the build's scratch is a fixed buffer of
+ * ZS_NOALLOC_SCRATCH_BYTES inside the library, one per device, held from the
+ * first call on that device until the process ends.  The call allocates and
+ * frees nothing; the caller still passes the inputs and outputs.
+ *
+ *   dst, n_edges, n_nodes, rowptr, perm, dst32, bad_flag, stream
+ *       as in zs_build_csr (same kernels, bitwise the same outputs).  The
+ *       buffers and the stream must belong to the calling thread's current
+ *       device.
+ *
+ * Returns ZS_ERR_SCRATCH, before any device work, when
+ * zs_csr_workspace_bytes(n_edges, n_nodes) > ZS_NOALLOC_SCRATCH_BYTES (at
+ * 4096 nodes about 3.3 million edges fit; at 16384 nodes the 2.6 million-edge
+ * frame needs 27.9 MiB).  Nothing in the buffer has to start at zero: every
+ * entry a build reads was written earlier in the same build.  All calls on
+ * one device share its buffer, so calls whose work overlaps on that device
+ * (other streams, other threads) race: serialize them.
+ */
+#define ZS_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int zs_build_csr_noalloc(const int64_t *dst, int64_t n_edges, int64_t n_nodes,
+                         int32_t *rowptr, int32_t *perm, int32_t *dst32,
+                         int32_t *bad_flag, void *stream);
 
 /*
  * zs_forward -- fused zonal scatter forward (same page, "What", Forward

@@ -9,6 +9,7 @@ import edge_node_scatter_amd as zs
 
 ZS_ERR_NULL, ZS_ERR_SHAPE, ZS_ERR_INDEX = -1, -2, -3
 ZS_ERR_UNSUPPORTED, ZS_ERR_ALIAS, ZS_ERR_WORKSPACE = -4, -5, -6
+ZS_ERR_SCRATCH = -8
 
 # Fake device addresses: every call below fails its host-side checks, so none
 # of these is ever dereferenced or handed to HIP.
@@ -28,7 +29,7 @@ def lib():
 def test_header_symbols_exported(lib):
     declared = zs.declared_symbols()
     assert set(declared) == {"zs_status_string", "zs_csr_workspace_bytes", "zs_build_csr",
-                             "zs_forward", "zs_backward", "zs_forward_strided",
+                             "zs_build_csr_noalloc", "zs_forward", "zs_backward", "zs_forward_strided",
                              "zs_backward_strided", "zs_forward_normalized",
                              "zs_backward_normalized"}
     out = subprocess.check_output(["nm", "-D", "--defined-only", zs.LIB_PATH], text=True)
@@ -39,7 +40,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert zs.status_string(s)
     assert zs.status_string(-99) == "unknown status"
 
@@ -69,6 +70,30 @@ def test_build_csr_rejects(lib):
     assert f(A, 10, 4, B, C_, D, W + 4, MB) == ZS_ERR_UNSUPPORTED   # workspace alignment
     assert f(A, 10, 4, B, C_, D, A, MB) == ZS_ERR_ALIAS            # workspace over dst
     assert f(A, 10, 4, B, C_, D, W, MB, W + 64) == ZS_ERR_ALIAS     # flag inside workspace
+
+
+def test_noalloc_limit_matches_the_header():
+    import re
+    m = re.search(r"#define ZS_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(zs.HEADER_PATH).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == zs.NOALLOC_SCRATCH_BYTES
+
+
+def test_build_csr_noalloc_rejects(lib):
+    """The same host checks as zs_build_csr, then the scratch limit: sizes whose
+    workspace exceeds the fixed buffer are refused before any HIP call."""
+    def f(dst, e, n, rowptr, perm, dst32, flag=None):
+        return lib.zs_build_csr_noalloc(dst, e, n, rowptr, perm, dst32, flag, None)
+    assert f(A, 10, 0, B, C_, D) == ZS_ERR_SHAPE
+    assert f(None, 10, 4, B, C_, D) == ZS_ERR_NULL
+    assert f(A + 4, 10, 4, B, C_, D) == ZS_ERR_UNSUPPORTED
+    assert f(A, 10, 4, A + 8, C_, D) == ZS_ERR_ALIAS
+    assert f(A, 10, 4, B, C_, D, C_ + 4) == ZS_ERR_ALIAS
+    limit = zs.NOALLOC_SCRATCH_BYTES
+    assert zs.zs_csr_workspace_bytes(2600000, 16384) <= limit     # the 16384-node frame fits
+    big = 5_000_000
+    assert zs.zs_csr_workspace_bytes(big, 4096) > limit
+    assert f(A, big, 4096, B, C_, D) == ZS_ERR_SCRATCH
+    assert "scratch" in zs.status_string(ZS_ERR_SCRATCH)
 
 
 def test_forward_rejects(lib):
