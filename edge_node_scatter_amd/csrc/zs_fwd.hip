@@ -329,9 +329,104 @@ __device__ __attribute__((always_inline)) inline void fwd_stage_accumulate(
     }
 }
 
-// NORM: also accumulate each node's envelope sum deg in edge order and write
+// One node of the staged forward, by the calling wavefront (lanes as above;
+// channel tile blockIdx.y).  rsh / csh: this wavefront's LDS staging
+// (FwdShape<VEC, B>::RAD float4 and B*16 floats).
+// NORM: also accumulate the node's envelope sum deg in edge order and write
 // y = out * norm with norm = 1/sqrt(deg) (0 for deg <= 0); out (the
 // unnormalised sum) is written only when the pointer is non-null.
+// The pad column csh[b*16 + 15] is read only as the weight of the lanes that
+// own the slot past row 15, whose sums are never stored (those lanes store
+// zeros into row 0), and carries the envelope factors with NORM.
+template <int VEC, int B, bool NORM>
+__device__ __attribute__((always_inline)) inline void fwd_staged_node(
+    int64_t node, int64_t k0, int64_t k1, const float* __restrict__ coupling,
+    const float* __restrict__ radial, const InLayout& L, const int32_t* __restrict__ perm,
+    int64_t n_edges, int64_t C, float* __restrict__ out, const NormIO& nio, float4* rsh,
+    float* csh) {
+    using S = FwdShape<VEC, B>;
+    static_assert(S::CV * 64 >= B * (kZonal + 1), "coupling and envelope slots");
+    static_assert(B <= 64, "one perm entry per lane");
+    const int lane = threadIdx.x & 63;
+    const int q = lane & 7;
+    const int j = lane >> 3;
+    const int rA = 2 * j + 1;                 // rows rA, rA + 1 (rA + 1 == 16 is row 0)
+    const int sA = row_slot(rA);
+    const int sB = row_slot(rA + 1 <= kZonal ? rA + 1 : kZonal);
+    const int64_t cbase = int64_t(blockIdx.y) * S::T;
+    const int64_t c0 = cbase + q * VEC;
+    const int n_valid = c0 >= C ? 0 : (C - c0 < VEC ? int(C - c0) : VEC);
+    const int64_t nb = (k1 - k0 + B - 1) / B;
+
+    float acc0[VEC], acc1[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc0[v] = acc1[v] = 0.0f;
+    float deg = 0.0f;
+    auto batch_count = [k0, k1](int64_t t) {
+        const int64_t kb = k0 + t * B;
+        return int(k1 - kb < B ? k1 - kb : B);
+    };
+
+    if (nb > 0) {
+        FwdRegs<VEC, B> RA, RB;
+        PermRaw pA = perm_issue(perm, k0, k1, lane, B);
+        PermRaw pB = perm_issue(perm, k0 + B, k1, lane, B);
+        fwd_fetch<VEC, B, NORM>(RA, lane, perm_resolve(pA, n_edges), coupling, radial, nio.env,
+                                L, C, cbase);
+        for (int64_t t = 0; t < nb; t += 2) {
+            const PermRaw pN = perm_issue(perm, k0 + (t + 2) * B, k1, lane, B);
+            fwd_fetch<VEC, B, NORM>(RB, lane, perm_resolve(pB, n_edges), coupling, radial,
+                                    nio.env, L, C, cbase);
+            fwd_stage_accumulate<VEC, B, NORM>(RA, rsh, csh, batch_count(t), lane, q, j, sA, sB,
+                                               acc0, acc1, deg);
+            if (t + 1 >= nb) break;
+            pB = perm_issue(perm, k0 + (t + 3) * B, k1, lane, B);
+            fwd_fetch<VEC, B, NORM>(RA, lane, perm_resolve(pN, n_edges), coupling, radial,
+                                    nio.env, L, C, cbase);
+            fwd_stage_accumulate<VEC, B, NORM>(RB, rsh, csh, batch_count(t + 1), lane, q, j, sA,
+                                               sB, acc0, acc1, deg);
+        }
+    }
+
+    float zero[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) zero[v] = 0.0f;
+    if (NORM) {
+        const float nrm = deg > 0.0f ? 1.0f / sqrtf(deg) : 0.0f;
+        if (lane == 0 && blockIdx.y == 0) nio.norm[node] = nrm;
+        float y0[VEC], y1[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            y0[v] = acc0[v] * nrm;
+            y1[v] = acc1[v] * nrm;
+        }
+        float* ynode = nio.y + node * kRows * C + c0;
+        row_store<VEC>(ynode + int64_t(rA) * C, y0, n_valid);
+        if (rA + 1 <= kZonal)
+            row_store<VEC>(ynode + int64_t(rA + 1) * C, y1, n_valid);
+        else
+            row_store<VEC>(ynode, zero, n_valid);
+    }
+    if (!NORM || out != nullptr) {
+        float* onode = out + node * kRows * C + c0;
+        row_store<VEC>(onode + int64_t(rA) * C, acc0, n_valid);
+        if (rA + 1 <= kZonal)
+            row_store<VEC>(onode + int64_t(rA + 1) * C, acc1, n_valid);
+        else
+            row_store<VEC>(onode, zero, n_valid);
+    }
+}
+
+// A node's CSR range [k0, k1), clamped to [0, n_edges].
+__device__ __attribute__((always_inline)) inline void node_range(const int32_t* __restrict__ rowptr,
+                                                                 int64_t node, int64_t n_edges,
+                                                                 int64_t& k0, int64_t& k1) {
+    k0 = rowptr[node];
+    k1 = rowptr[node + 1];
+    k0 = k0 < 0 ? 0 : (k0 > n_edges ? n_edges : k0);
+    k1 = k1 < k0 ? k0 : (k1 > n_edges ? n_edges : k1);
+}
+
 template <int VEC, int B, bool NORM>
 __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restrict__ coupling,
                                                            const float* __restrict__ radial,
@@ -341,88 +436,14 @@ __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restri
                                                            int64_t n_nodes, int64_t n_edges,
                                                            int64_t C, float* __restrict__ out,
                                                            NormIO nio) {
-    using S = FwdShape<VEC, B>;
-    static_assert(S::CV * 64 >= B * (kZonal + 1), "coupling and envelope slots");
-    static_assert(B <= 64, "one perm entry per lane");
-    __shared__ float4 rsh[S::RAD];
+    __shared__ float4 rsh[FwdShape<VEC, B>::RAD];
     __shared__ float csh[B * 16];
-
-    const int lane = threadIdx.x;
-    const int q = lane & 7;
-    const int j = lane >> 3;
-    const int rA = 2 * j + 1;                 // rows rA, rA + 1 (rA + 1 == 16 is row 0)
-    const int sA = row_slot(rA);
-    const int sB = row_slot(rA + 1 <= kZonal ? rA + 1 : kZonal);
-    const int64_t cbase = int64_t(blockIdx.y) * S::T;
-    const int64_t c0 = cbase + q * VEC;
-    const int n_valid = c0 >= C ? 0 : (C - c0 < VEC ? int(C - c0) : VEC);
-
-    if (lane < B) csh[lane * 16 + 15] = 0.0f;   // pad column, never fetched
-
+    if (threadIdx.x < B) csh[threadIdx.x * 16 + 15] = 0.0f;   // pad column, never fetched
     for (int64_t node = blockIdx.x; node < n_nodes; node += gridDim.x) {
-        int64_t k0 = rowptr[node];
-        int64_t k1 = rowptr[node + 1];
-        k0 = k0 < 0 ? 0 : (k0 > n_edges ? n_edges : k0);
-        k1 = k1 < k0 ? k0 : (k1 > n_edges ? n_edges : k1);
-        const int64_t nb = (k1 - k0 + B - 1) / B;
-
-        float acc0[VEC], acc1[VEC];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) acc0[v] = acc1[v] = 0.0f;
-        float deg = 0.0f;
-        auto batch_count = [k0, k1](int64_t t) {
-            const int64_t kb = k0 + t * B;
-            return int(k1 - kb < B ? k1 - kb : B);
-        };
-
-        if (nb > 0) {
-            FwdRegs<VEC, B> RA, RB;
-            PermRaw pA = perm_issue(perm, k0, k1, lane, B);
-            PermRaw pB = perm_issue(perm, k0 + B, k1, lane, B);
-            fwd_fetch<VEC, B, NORM>(RA, lane, perm_resolve(pA, n_edges), coupling, radial,
-                                    nio.env, L, C, cbase);
-            for (int64_t t = 0; t < nb; t += 2) {
-                const PermRaw pN = perm_issue(perm, k0 + (t + 2) * B, k1, lane, B);
-                fwd_fetch<VEC, B, NORM>(RB, lane, perm_resolve(pB, n_edges), coupling, radial,
-                                        nio.env, L, C, cbase);
-                fwd_stage_accumulate<VEC, B, NORM>(RA, rsh, csh, batch_count(t), lane, q, j, sA,
-                                                   sB, acc0, acc1, deg);
-                if (t + 1 >= nb) break;
-                pB = perm_issue(perm, k0 + (t + 3) * B, k1, lane, B);
-                fwd_fetch<VEC, B, NORM>(RA, lane, perm_resolve(pN, n_edges), coupling, radial,
-                                        nio.env, L, C, cbase);
-                fwd_stage_accumulate<VEC, B, NORM>(RB, rsh, csh, batch_count(t + 1), lane, q, j,
-                                                   sA, sB, acc0, acc1, deg);
-            }
-        }
-
-        float zero[VEC];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) zero[v] = 0.0f;
-        if (NORM) {
-            const float nrm = deg > 0.0f ? 1.0f / sqrtf(deg) : 0.0f;
-            if (lane == 0 && blockIdx.y == 0) nio.norm[node] = nrm;
-            float y0[VEC], y1[VEC];
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-                y0[v] = acc0[v] * nrm;
-                y1[v] = acc1[v] * nrm;
-            }
-            float* ynode = nio.y + node * kRows * C + c0;
-            row_store<VEC>(ynode + int64_t(rA) * C, y0, n_valid);
-            if (rA + 1 <= kZonal)
-                row_store<VEC>(ynode + int64_t(rA + 1) * C, y1, n_valid);
-            else
-                row_store<VEC>(ynode, zero, n_valid);
-        }
-        if (!NORM || out != nullptr) {
-            float* onode = out + node * kRows * C + c0;
-            row_store<VEC>(onode + int64_t(rA) * C, acc0, n_valid);
-            if (rA + 1 <= kZonal)
-                row_store<VEC>(onode + int64_t(rA + 1) * C, acc1, n_valid);
-            else
-                row_store<VEC>(onode, zero, n_valid);
-        }
+        int64_t k0, k1;
+        node_range(rowptr, node, n_edges, k0, k1);
+        fwd_staged_node<VEC, B, NORM>(node, k0, k1, coupling, radial, L, perm, n_edges, C, out,
+                                      nio, rsh, csh);
     }
 }
 
@@ -450,6 +471,134 @@ struct SlotShape {
     static constexpr int CV = (CW + 63) / 64;
 };
 
+// One node's slot s (rows of degree s + 1) of the slot-split forward, by the
+// calling wavefront (lane = j*8 + q; channel tile blockIdx.y).  rsh / csh:
+// this wavefront's LDS staging (SlotShape<VEC, B>::RAD float4 and ::CW
+// floats).
+template <int VEC, int B, bool NORM>
+__device__ __attribute__((always_inline)) inline void fwd_slot_node(
+    int64_t node, int s, int64_t k0, int64_t k1, const float* __restrict__ coupling,
+    const float* __restrict__ radial, const InLayout& L, const int32_t* __restrict__ perm,
+    int64_t n_edges, int64_t C, float* __restrict__ out, const NormIO& nio, float4* rsh,
+    float* csh) {
+    using S = SlotShape<VEC, B>;
+    static_assert(B <= 64, "one perm entry per lane");
+    const int lane = threadIdx.x & 63;
+    const int l = s + 1;
+    const int r0 = l * l;                      // first row of the slot
+    const int nr = 2 * l + 1;                  // rows of the slot
+    const int q = lane & 7;
+    const int j = lane >> 3;
+    const int64_t cbase = int64_t(blockIdx.y) * S::T;
+    const int64_t c0 = cbase + q * VEC;
+    const int n_valid = c0 >= C ? 0 : (C - c0 < VEC ? int(C - c0) : VEC);
+    const int64_t slot_off = int64_t(s) * L.rad_slot;
+    const int64_t nb = (k1 - k0 + B - 1) / B;
+
+    float acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
+    float deg = 0.0f;
+
+    // Loads of one batch: radial float4 f = i*64 + lane is batch edge
+    // f / F4, float4 f % F4 of the tile's slot row; coupling float
+    // idx = i*64 + lane is batch edge idx / 8, column idx % 8 of the slot
+    // (column 7, never a row of the slot, carries the envelope factor
+    // with NORM).  Absent edges, channels and columns read a valid
+    // substitute (edge 0, the tile's first channel, the slot's first
+    // column) that is never used.
+    auto fetch = [&](float4 (&rr)[S::RV], float (&ww)[S::CV], int pe) {
+#pragma unroll
+        for (int i = 0; i < S::RV; ++i) {
+            const int f = i * 64 + lane;
+            const int e = __shfl(pe, f < S::RAD ? f / S::F4 : 0, 64);
+            const int64_t es = e >= 0 ? e : 0;
+            const int64_t ch = cbase + (f % S::F4) * 4;
+            const int64_t cs = ch < C ? ch : cbase;
+            rr[i] = load_stream4<ZS_FWD_NT != 0>(radial + es * L.rad_edge + slot_off + cs);
+        }
+#pragma unroll
+        for (int i = 0; i < S::CV; ++i) {
+            const int idx = i * 64 + lane;
+            const int b = idx < S::CW ? idx >> 3 : 0;
+            const int col = idx & 7;
+            const int e = __shfl(pe, b, 64);
+            const int64_t es = e >= 0 ? e : 0;
+            const bool in_env = NORM && col == 7;
+            ww[i] = in_env ? nio.env[es]
+                           : coupling[es * L.cpl_edge + (r0 - 1) + (col < nr ? col : 0)];
+        }
+    };
+    auto stage_accumulate = [&](const float4 (&rr)[S::RV], const float (&ww)[S::CV], int cnt) {
+        wave_lds_sync();   // the previous batch's reads come before these writes
+#pragma unroll
+        for (int i = 0; i < S::RV; ++i)
+            if (S::RAD % 64 == 0 || i * 64 + lane < S::RAD) rsh[i * 64 + lane] = rr[i];
+#pragma unroll
+        for (int i = 0; i < S::CV; ++i)
+            if (S::CW % 64 == 0 || i * 64 + lane < S::CW) csh[i * 64 + lane] = ww[i];
+        wave_lds_sync();   // every lane reads values other lanes staged
+        const float* rf = reinterpret_cast<const float*>(rsh);
+        const int jw = j < nr ? j : 0;
+        auto edge = [&](int b) {
+            if (NORM) deg = deg + csh[b * 8 + 7];
+            float x[VEC];
+            lds_read<VEC>(rf + b * S::T + q * VEC, x);
+            const float w = csh[b * 8 + jw];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const float m = w * x[v];
+                acc[v] = acc[v] + m;
+            }
+        };
+        if (cnt == B) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) edge(b);
+        } else {
+            for (int b = 0; b < cnt; ++b) edge(b);
+        }
+    };
+    auto batch_count = [k0, k1](int64_t t) {
+        const int64_t kb = k0 + t * B;
+        return int(k1 - kb < B ? k1 - kb : B);
+    };
+
+    if (nb > 0) {
+        float4 RA[S::RV], RB[S::RV];
+        float WA[S::CV], WB[S::CV];
+        PermRaw pA = perm_issue(perm, k0, k1, lane, B);
+        PermRaw pB = perm_issue(perm, k0 + B, k1, lane, B);
+        fetch(RA, WA, perm_resolve(pA, n_edges));
+        for (int64_t t = 0; t < nb; t += 2) {
+            const PermRaw pN = perm_issue(perm, k0 + (t + 2) * B, k1, lane, B);
+            fetch(RB, WB, perm_resolve(pB, n_edges));
+            stage_accumulate(RA, WA, batch_count(t));
+            if (t + 1 >= nb) break;
+            pB = perm_issue(perm, k0 + (t + 3) * B, k1, lane, B);
+            fetch(RA, WA, perm_resolve(pN, n_edges));
+            stage_accumulate(RB, WB, batch_count(t + 1));
+        }
+    }
+
+    float zero[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) zero[v] = 0.0f;
+    const int64_t row_off = node * kRows * C + c0;
+    if (NORM) {
+        const float nrm = deg > 0.0f ? 1.0f / sqrtf(deg) : 0.0f;
+        if (s == 0 && lane == 0 && blockIdx.y == 0) nio.norm[node] = nrm;
+        float y[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) y[v] = acc[v] * nrm;
+        if (j < nr) row_store<VEC>(nio.y + row_off + int64_t(r0 + j) * C, y, n_valid);
+        else if (s == 0 && j == nr) row_store<VEC>(nio.y + row_off, zero, n_valid);
+    }
+    if (!NORM || out != nullptr) {
+        if (j < nr) row_store<VEC>(out + row_off + int64_t(r0 + j) * C, acc, n_valid);
+        else if (s == 0 && j == nr) row_store<VEC>(out + row_off, zero, n_valid);
+    }
+}
+
 template <int VEC, int B, bool NORM>
 __global__ __launch_bounds__(192) void zs_fwd_slot_kernel(const float* __restrict__ coupling,
                                                           const float* __restrict__ radial,
@@ -460,134 +609,14 @@ __global__ __launch_bounds__(192) void zs_fwd_slot_kernel(const float* __restric
                                                           int64_t C, float* __restrict__ out,
                                                           NormIO nio) {
     using S = SlotShape<VEC, B>;
-    static_assert(B <= 64, "one perm entry per lane");
     __shared__ float4 rsh_all[kSlots][S::RAD];
     __shared__ float csh_all[kSlots][S::CW];
-
     const int s = threadIdx.x >> 6;            // slot of this wavefront
-    const int lane = threadIdx.x & 63;
-    const int l = s + 1;
-    const int r0 = l * l;                      // first row of the slot
-    const int nr = 2 * l + 1;                  // rows of the slot
-    const int q = lane & 7;
-    const int j = lane >> 3;
-    float4* rsh = rsh_all[s];
-    float* csh = csh_all[s];
-    const int64_t cbase = int64_t(blockIdx.y) * S::T;
-    const int64_t c0 = cbase + q * VEC;
-    const int n_valid = c0 >= C ? 0 : (C - c0 < VEC ? int(C - c0) : VEC);
-    const int64_t slot_off = int64_t(s) * L.rad_slot;
-
     for (int64_t node = blockIdx.x; node < n_nodes; node += gridDim.x) {
-        int64_t k0 = rowptr[node];
-        int64_t k1 = rowptr[node + 1];
-        k0 = k0 < 0 ? 0 : (k0 > n_edges ? n_edges : k0);
-        k1 = k1 < k0 ? k0 : (k1 > n_edges ? n_edges : k1);
-        const int64_t nb = (k1 - k0 + B - 1) / B;
-
-        float acc[VEC];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
-        float deg = 0.0f;
-
-        // Loads of one batch: radial float4 f = i*64 + lane is batch edge
-        // f / F4, float4 f % F4 of the tile's slot row; coupling float
-        // idx = i*64 + lane is batch edge idx / 8, column idx % 8 of the slot
-        // (column 7, never a row of the slot, carries the envelope factor
-        // with NORM).  Absent edges, channels and columns read a valid
-        // substitute (edge 0, the tile's first channel, the slot's first
-        // column) that is never used.
-        auto fetch = [&](float4 (&rr)[S::RV], float (&ww)[S::CV], int pe) {
-#pragma unroll
-            for (int i = 0; i < S::RV; ++i) {
-                const int f = i * 64 + lane;
-                const int e = __shfl(pe, f < S::RAD ? f / S::F4 : 0, 64);
-                const int64_t es = e >= 0 ? e : 0;
-                const int64_t ch = cbase + (f % S::F4) * 4;
-                const int64_t cs = ch < C ? ch : cbase;
-                rr[i] = load_stream4<ZS_FWD_NT != 0>(radial + es * L.rad_edge + slot_off + cs);
-            }
-#pragma unroll
-            for (int i = 0; i < S::CV; ++i) {
-                const int idx = i * 64 + lane;
-                const int b = idx < S::CW ? idx >> 3 : 0;
-                const int col = idx & 7;
-                const int e = __shfl(pe, b, 64);
-                const int64_t es = e >= 0 ? e : 0;
-                const bool in_env = NORM && col == 7;
-                ww[i] = in_env ? nio.env[es]
-                               : coupling[es * L.cpl_edge + (r0 - 1) + (col < nr ? col : 0)];
-            }
-        };
-        auto stage_accumulate = [&](const float4 (&rr)[S::RV], const float (&ww)[S::CV],
-                                    int cnt) {
-            wave_lds_sync();   // the previous batch's reads come before these writes
-#pragma unroll
-            for (int i = 0; i < S::RV; ++i)
-                if (S::RAD % 64 == 0 || i * 64 + lane < S::RAD) rsh[i * 64 + lane] = rr[i];
-#pragma unroll
-            for (int i = 0; i < S::CV; ++i)
-                if (S::CW % 64 == 0 || i * 64 + lane < S::CW) csh[i * 64 + lane] = ww[i];
-            wave_lds_sync();   // every lane reads values other lanes staged
-            const float* rf = reinterpret_cast<const float*>(rsh);
-            const int jw = j < nr ? j : 0;
-            auto edge = [&](int b) {
-                if (NORM) deg = deg + csh[b * 8 + 7];
-                float x[VEC];
-                lds_read<VEC>(rf + b * S::T + q * VEC, x);
-                const float w = csh[b * 8 + jw];
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) {
-                    const float m = w * x[v];
-                    acc[v] = acc[v] + m;
-                }
-            };
-            if (cnt == B) {
-#pragma unroll
-                for (int b = 0; b < B; ++b) edge(b);
-            } else {
-                for (int b = 0; b < cnt; ++b) edge(b);
-            }
-        };
-        auto batch_count = [k0, k1](int64_t t) {
-            const int64_t kb = k0 + t * B;
-            return int(k1 - kb < B ? k1 - kb : B);
-        };
-
-        if (nb > 0) {
-            float4 RA[S::RV], RB[S::RV];
-            float WA[S::CV], WB[S::CV];
-            PermRaw pA = perm_issue(perm, k0, k1, lane, B);
-            PermRaw pB = perm_issue(perm, k0 + B, k1, lane, B);
-            fetch(RA, WA, perm_resolve(pA, n_edges));
-            for (int64_t t = 0; t < nb; t += 2) {
-                const PermRaw pN = perm_issue(perm, k0 + (t + 2) * B, k1, lane, B);
-                fetch(RB, WB, perm_resolve(pB, n_edges));
-                stage_accumulate(RA, WA, batch_count(t));
-                if (t + 1 >= nb) break;
-                pB = perm_issue(perm, k0 + (t + 3) * B, k1, lane, B);
-                fetch(RA, WA, perm_resolve(pN, n_edges));
-                stage_accumulate(RB, WB, batch_count(t + 1));
-            }
-        }
-
-        float zero[VEC];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) zero[v] = 0.0f;
-        const int64_t row_off = node * kRows * C + c0;
-        if (NORM) {
-            const float nrm = deg > 0.0f ? 1.0f / sqrtf(deg) : 0.0f;
-            if (s == 0 && lane == 0 && blockIdx.y == 0) nio.norm[node] = nrm;
-            float y[VEC];
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) y[v] = acc[v] * nrm;
-            if (j < nr) row_store<VEC>(nio.y + row_off + int64_t(r0 + j) * C, y, n_valid);
-            else if (s == 0 && j == nr) row_store<VEC>(nio.y + row_off, zero, n_valid);
-        }
-        if (!NORM || out != nullptr) {
-            if (j < nr) row_store<VEC>(out + row_off + int64_t(r0 + j) * C, acc, n_valid);
-            else if (s == 0 && j == nr) row_store<VEC>(out + row_off, zero, n_valid);
-        }
+        int64_t k0, k1;
+        node_range(rowptr, node, n_edges, k0, k1);
+        fwd_slot_node<VEC, B, NORM>(node, s, k0, k1, coupling, radial, L, perm, n_edges, C, out,
+                                    nio, rsh_all[s], csh_all[s]);
     }
 }
 

@@ -20,6 +20,7 @@ import torch
 import edge_node_scatter_amd as zs
 import oracle
 import synthetic
+from cases import heavy_destinations
 
 pytestmark = pytest.mark.gpu
 ATOL, RTOL = 1e-6, 1e-5
@@ -122,13 +123,29 @@ NORM_CASES = [
     ("n2500_batch8", 2500, 40000, 32, "uniform"),
     ("staged_c48", 1300, 30000, 48, "uniform"),     # one-wavefront-per-tile forward, 6 ch/lane
     ("slot_b8", 1500, 30000, 32, "uniform"),        # slot-split forward, 8-edge batches
+    # heavy nodes (several thousand edges) beside light ones, envelope sums included
+    ("split_c32", 3000, 200000, 32, "heavy"),
+    ("split_c16", 2600, 150000, 16, "heavy"),
+    ("split_c8", 2600, 120000, 8, "heavy"),
+    ("split_grid_stride_c8", 1_100_000, 2_300_000, 8, "heavy"),
 ]
 
 
 @pytest.mark.parametrize("label,N,E,C,kind", NORM_CASES, ids=[c[0] for c in NORM_CASES])
 def test_normalized_shapes(dev, label, N, E, C, kind):
-    w = synthetic.custom(label, N, E, C, seed=9100 + E, dst_kind=kind, envelope=True)
-    run_and_compare(synthetic.make_inputs(w), N, dev, label)
+    w = synthetic.custom(label, N, E, C, seed=9100 + E,
+                         dst_kind="uniform" if kind == "heavy" else kind, envelope=True)
+    x = synthetic.make_inputs(w)
+    if kind == "heavy":
+        x["dst"] = heavy_destinations(E, N, seed=E + C)
+    run_and_compare(x, N, dev, label)
+
+
+def test_normalized_large(dev):
+    """The 16384-node, C = 64 frame (E = 2.6M) through the normalised pair,
+    compared with the oracle in full."""
+    w = synthetic.WORKLOADS["large"]
+    run_and_compare(synthetic.make_inputs(w), w.n_nodes, dev, "large")
 
 
 def test_normalized_without_out(dev):

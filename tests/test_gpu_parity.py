@@ -20,6 +20,7 @@ import torch
 import edge_node_scatter_amd as zs
 import oracle
 import synthetic
+from cases import heavy_destinations
 
 pytestmark = pytest.mark.gpu
 ATOL, RTOL = 1e-6, 1e-5
@@ -192,7 +193,20 @@ EDGE_CASES = [
     # backward work items = 2^18 nodes): the kernels' grid-stride node loops.
     ("grid_stride_c8", 1_200_000, 2_400_000, 8, "uniform"),
     ("grid_stride_c16", 1_100_000, 1_500_000, 16, "uniform"),
+    # Heavy nodes (degree at least 1.5x the mean, up to several thousand
+    # edges) beside light ones in launches of the one-wavefront-per-node
+    # forward and the split-item backward, at each channel width up to 4 per
+    # lane, and on both sides of the grid-stride pass.
+    ("split_c32", 3000, 200000, 32, "heavy"),
+    ("split_c28", 2600, 150000, 28, "heavy"),
+    ("split_c24", 2600, 150000, 24, "heavy"),
+    ("split_c16", 2600, 150000, 16, "heavy"),
+    ("split_c12", 2600, 120000, 12, "heavy"),
+    ("split_c8", 2600, 120000, 8, "heavy"),
+    ("split_c4", 2600, 100000, 4, "heavy"),
+    ("split_grid_stride_c8", 1_100_000, 2_300_000, 8, "heavy"),
 ]
+
 
 
 @pytest.mark.parametrize("label,N,E,C,kind", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
@@ -202,6 +216,11 @@ def test_edge_cases(dev, label, N, E, C, kind):
     if kind == "skewed_small":
         rng = np.random.default_rng(5)
         x["dst"] = np.where(rng.random(E) < 0.7, rng.integers(0, 10, E), rng.integers(0, N, E))
+    elif kind == "heavy":
+        x["dst"] = heavy_destinations(E, N, seed=len(label) + C)
+        deg = np.bincount(x["dst"], minlength=N)
+        hmin = max(64, -(-3 * E // (2 * N)))
+        assert np.count_nonzero(deg >= hmin) >= 3 and deg[N - 1] >= hmin
     say(f"[gpu] edge case {label}: N={N} E={E} C={C}")
     res = run_gpu(x, dev, N)
     compare_full(x, res, N, label)
