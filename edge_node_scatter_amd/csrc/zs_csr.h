@@ -8,18 +8,16 @@ namespace zs {
 
 // ---- CSR build ------------------------------------------------------------
 struct CsrPlan {
-    int64_t tiles;        // edge tiles of the bucket level
-    int64_t tile_edges;   // edges per tile (last tile may be shorter)
+    int64_t chunks;       // W: edge chunks sorted by the first kernel
+    int64_t chunk_edges;  // edges per chunk (the last may be shorter)
     int bucket_shift;     // SB: a bucket holds 2^SB consecutive nodes
     int bucket_bits;      // ceil(log2(buckets))
     int64_t buckets;      // NB
     bool node_lds;        // per-bucket node tables fit in LDS
     size_t off_flag;      // int32 error flag
-    size_t off_tile_bad;  // int32 [tiles] per-tile out-of-range indicator
-    size_t off_counts;    // int32 [tiles][buckets] per-tile counts, then offsets
-    size_t off_tot;       // int32 [buckets] bucket totals
-    size_t off_starts;    // int32 [buckets + 1] bucket starts
-    size_t off_pairs;     // int2 [n_edges] (destination, edge) grouped by bucket
+    size_t off_chunk_bad; // int32 [W] per-chunk out-of-range indicator
+    size_t off_loff;      // int32 [W][NB + 1] offset of each bucket's run in each chunk
+    size_t off_pairs;     // int2 [n_edges] (destination, edge), chunk-major, bucket runs
     size_t off_scratch;   // int32 [n_nodes] node offsets (only without node_lds)
     size_t bytes;         // total workspace bytes
 };

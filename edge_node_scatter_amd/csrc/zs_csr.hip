@@ -3,33 +3,32 @@
 // The fused forward walks each node's edges in the order index_add would add
 // them, i.e. increasing edge id (deepmd-kit PR #6072, "fused Triton zonal
 // scatter for the GIE head", section "What", last bullet).  This file builds
-// that CSR with a deterministic two-level counting sort; no result depends on
-// the order in which atomics land.
+// that CSR with a deterministic two-level counting sort in two kernels; no
+// result depends on the order in which atomics land.
 //
 // Nodes are grouped into NB <= 1024 buckets of BN = 2^SB consecutive nodes
-// (BN = 8 up to 8192 nodes).
+// (NB <= 256 while a bucket's node tables fit in LDS), the edges into W
+// chunks of consecutive edge ids.
 //
-//   1. bucket_count  one workgroup per edge tile histograms the tile's bucket
-//                    ids in LDS and records whether the tile held an
-//                    out-of-range destination;
-//   2. bucket_scan   per bucket, the exclusive scan of the per-tile counts over
-//                    tiles and the bucket's total; folds the out-of-range bits
-//                    into the flag;
-//   3. bucket_place  per tile: bucket starts (scan of the totals; tile 0 also
-//                    writes them out) plus the tile's offsets give each
-//                    bucket's running offset; the tile
-//                    is split into 4 parts (one wavefront each, with per-part
-//                    histograms so the parts start at the right offsets); lanes
-//                    with equal bucket ids are matched with ballots and ranked
-//                    by lane order.  Writes (destination, edge) pairs grouped by
-//                    bucket, in increasing edge id within each bucket, and dst32;
-//   4. node_place    one workgroup per bucket reads its contiguous run of pairs,
-//                    histograms the local node ids (4 parts, per-part counts),
-//                    writes rowptr for its nodes and places perm the same way.
+//   1. chunk_sort   one 1024-thread workgroup per chunk: validates the
+//                   destinations (dst32 = -1 where out of range), sorts the
+//                   chunk's edges stably by bucket inside the chunk's own
+//                   region of the pairs array (16 parts, one wavefront each;
+//                   per-part histograms give each part its offsets; lanes with
+//                   equal bucket ids are matched with ballots and ranked by
+//                   lane order) and writes the offset of every bucket's run in
+//                   the chunk, loff[c][b] (loff[c][NB] = the chunk's valid
+//                   edges).
+//   2. bucket_place one workgroup per bucket b: its edges, in increasing edge
+//                   id, are the runs [loff[c][b], loff[c][b + 1]) of chunks
+//                   c = 0, 1, ... in turn, and the bucket's first CSR position
+//                   is sum over c of loff[c][b] (every valid edge of a lower
+//                   bucket sits before b's run in its chunk).  The workgroup
+//                   gathers its runs, histograms the local node ids, writes
+//                   rowptr for its nodes and places perm stably the same way.
 //
-// Both levels are stable, so perm lists each node's edges in increasing edge
-// id.  Traffic is a few int32/int64 passes over the edges; the per-tile count
-// matrix is tiles x NB entries, far smaller than tiles x N.
+// Neither kernel reads more than a column pair of the W x NB offset table, so
+// every workgroup is a few memory round trips deep.
 //
 // Every destination is range-checked; an out-of-range one is never used as an
 // index and raises the validation flag.
@@ -39,18 +38,30 @@ namespace zs {
 
 namespace {
 
-constexpr int kThreads = 256;                // every CSR kernel: 4 wavefronts
-constexpr int kParts = kThreads / 64;        // wavefronts that place a tile / bucket
-constexpr int kAhead = 8;                    // 64-edge steps whose keys are held at once
-constexpr int64_t kTileEdgesMin = 1024;      // 4 steps per wavefront
-constexpr int64_t kTilesMax = 4096;
-constexpr int64_t kCountBudget = int64_t(1) << 21;   // tiles x buckets entries (8 MiB)
-#ifndef ZS_CSR_BUCKET_BITS
-#define ZS_CSR_BUCKET_BITS 10
+#ifndef ZS_CSR_THREADS
+#define ZS_CSR_THREADS 1024
 #endif
-constexpr int kBucketsMaxBits = ZS_CSR_BUCKET_BITS;   // NB <= 1024 (LDS tables <= 20 KiB)
-constexpr int kBucketMinBits = 3;            // BN >= 8
-constexpr int kNodeLdsMax = 2048;            // BN handled with LDS tables
+#ifndef ZS_CSR_CHUNK
+#define ZS_CSR_CHUNK 0   // 0: by frame size (below)
+#endif
+#ifndef ZS_CSR_BUCKET_BITS
+#define ZS_CSR_BUCKET_BITS 8
+#endif
+constexpr int kThreads = ZS_CSR_THREADS;     // both kernels' LDS path
+constexpr int kParts = kThreads / 64;        // wavefronts that sort a chunk / place a bucket
+constexpr int kGlobalThreads = 256;          // bucket_place with node tables in global memory
+constexpr int kAhead = 8;                    // 64-edge steps whose keys are held at once
+// Chunk length: 4096 edges from 2^19 edges on (measured, per build: the
+// 4096-node frames 26 vs 28 us, the 16384-node frame 75 vs 81 us against
+// 2048), 2048 below (the 1000-node frame 18 vs 19 us); longer when the frame
+// has more than kChunksMax such chunks.
+constexpr int64_t kChunkEdgesSmall = ZS_CSR_CHUNK > 0 ? ZS_CSR_CHUNK : 2048;
+constexpr int64_t kChunkEdgesLarge = ZS_CSR_CHUNK > 0 ? ZS_CSR_CHUNK : 4096;
+constexpr int64_t kChunkLargeFrom = int64_t(1) << 19;
+constexpr int64_t kChunksMax = 4096;
+constexpr int kBucketBitsSmall = ZS_CSR_BUCKET_BITS;   // NB <= 2^this while BN fits the LDS tables
+constexpr int kBucketBitsMax = 10;           // NB <= 1024
+constexpr int kNodeLdsMax = 512;             // BN handled with LDS tables
 
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
@@ -74,12 +85,13 @@ __device__ inline int32_t wave_inclusive_scan(int32_t v) {
     return v;
 }
 
-// In-place exclusive scan of a[0..n) (LDS) by the whole workgroup; returns the
-// total.  Each thread scans a contiguous run of entries.
+// In-place exclusive scan of a[0..n) (LDS) by the whole workgroup of TH
+// threads; returns the total.  Each thread scans a contiguous run of entries.
+template <int TH>
 __device__ inline int32_t block_exclusive_scan_lds(int32_t* a, int64_t n) {
-    __shared__ int32_t wave_tot[kThreads / 64];
+    __shared__ int32_t wave_tot[TH / 64];
     const int tid = threadIdx.x;
-    const int64_t per = (n + kThreads - 1) / kThreads;
+    const int64_t per = (n + TH - 1) / TH;
     const int64_t lo = tid * per < n ? tid * per : n;
     const int64_t hi = lo + per < n ? lo + per : n;
     int32_t local = 0;
@@ -93,7 +105,7 @@ __device__ inline int32_t block_exclusive_scan_lds(int32_t* a, int64_t n) {
     if (lane == 63) wave_tot[wave] = incl;
     __syncthreads();
     int32_t off = 0, total = 0;
-    for (int w = 0; w < kThreads / 64; ++w) {
+    for (int w = 0; w < TH / 64; ++w) {
         if (w < wave) off += wave_tot[w];
         total += wave_tot[w];
     }
@@ -103,22 +115,18 @@ __device__ inline int32_t block_exclusive_scan_lds(int32_t* a, int64_t n) {
     return total;
 }
 
-// dst[0..n) (LDS) <- src[0..n) (global), 16 loads per thread in flight.
-__device__ inline void lds_load(int32_t* dst, const int32_t* __restrict__ src, int64_t n) {
-    constexpr int U = 16;
-    for (int64_t base = 0; base < n; base += int64_t(kThreads) * U) {
-        int32_t v[U];
+// Sum of v over the workgroup of TH threads (every thread gets it).
+template <int TH>
+__device__ inline int64_t block_sum(int64_t v) {
+    __shared__ int64_t part[TH / 64];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = base + int64_t(u) * kThreads + threadIdx.x;
-            v[u] = i < n ? src[i] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = base + int64_t(u) * kThreads + threadIdx.x;
-            if (i < n) dst[i] = v[u];
-        }
-    }
+    for (int h = 32; h >= 1; h >>= 1) v += __shfl_xor(v, h, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int64_t s = 0;
+    for (int w = 0; w < TH / 64; ++w) s += part[w];
+    __syncthreads();
+    return s;
 }
 
 // Lanes of the wavefront whose `key` (bits bits wide) equals this lane's,
@@ -133,346 +141,321 @@ __device__ inline uint64_t match_key(bool ok, int32_t key, int bits) {
     return same;
 }
 
-// ---- level 1: buckets of BN consecutive nodes -------------------------------
-
-__global__ __launch_bounds__(kThreads) void csr_bucket_count_kernel(
-    const int64_t* __restrict__ dst, int64_t n_edges, int64_t n_nodes, int64_t tile_edges,
-    int sb, int64_t n_buckets, int32_t* __restrict__ counts, int32_t* __restrict__ tile_bad) {
-    extern __shared__ int32_t bins[];
-    const int64_t t = blockIdx.x;
-    const int64_t e0 = t * tile_edges;
-    const int64_t e1 = e0 + tile_edges < n_edges ? e0 + tile_edges : n_edges;
-    for (int64_t i = threadIdx.x; i < n_buckets; i += kThreads) bins[i] = 0;
-    __syncthreads();
-    int bad = 0;
-    constexpr int U = 8;   // loads issued before the first is consumed
-    for (int64_t chunk = e0; chunk < e1; chunk += int64_t(kThreads) * U) {
-        int64_t keys[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t e = chunk + int64_t(u) * kThreads + threadIdx.x;
-            keys[u] = e < e1 ? dst[e] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t e = chunk + int64_t(u) * kThreads + threadIdx.x;
-            if (e >= e1) continue;
-            const int64_t key = keys[u];
-            if (key >= 0 && key < n_nodes)
-                atomicAdd(&bins[key >> sb], 1);
-            else
-                bad = 1;
-        }
-    }
-    bad = __syncthreads_or(bad);
-    if (threadIdx.x == 0) tile_bad[t] = bad;
-    int32_t* row = counts + t * n_buckets;
-    for (int64_t i = threadIdx.x; i < n_buckets; i += kThreads) row[i] = bins[i];
-}
-
-// Per bucket: counts[t][b] <- sum_{t' < t} counts[t'][b] and tot[b] <- total.
-// Workgroup = kColBuckets buckets x kColChunks tile chunks; each thread sums
-// its chunk, the chunk sums are scanned in LDS, then the thread walks its
-// chunk again (now from the cache) rewriting it as exclusive offsets.  Block 0
-// also folds the per-tile out-of-range bits into the flag.  Up to
-// kColFewTiles tiles, 4 buckets per workgroup (four times the workgroups for
-// short columns: the 1000-node frame's whole build 25.2 vs 27.6 us, the
-// 4096-node frames' within the run-to-run spread); longer columns keep 16 (the
-// 16384-node frame's 2048 tiles: 81.6 us, against 102.9 us with 4).
-constexpr int kColChunks = 64;
-constexpr int64_t kColFewTiles = 1024;
-template <int kColBuckets>
-__global__ __launch_bounds__(kColBuckets * kColChunks) void csr_bucket_scan_kernel(
-    int32_t* __restrict__ counts, int64_t tiles, int64_t n_buckets, int32_t* __restrict__ tot,
-    const int32_t* __restrict__ tile_bad, int32_t* __restrict__ flag) {
-    __shared__ int32_t chunk_sum[kColChunks][kColBuckets];
-    const int i = threadIdx.x % kColBuckets;
-    const int c = threadIdx.x / kColBuckets;
-    const int64_t b = int64_t(blockIdx.x) * kColBuckets + i;
-    const int64_t t_lo = tiles * c / kColChunks;
-    const int64_t t_hi = tiles * (c + 1) / kColChunks;
-    int32_t sum = 0;
-    if (b < n_buckets) {
-#pragma unroll 8
-        for (int64_t t = t_lo; t < t_hi; ++t) sum += counts[t * n_buckets + b];
-    }
-    chunk_sum[c][i] = sum;
-    __syncthreads();
-    int32_t run = 0, total = 0;
-    for (int cc = 0; cc < kColChunks; ++cc) {
-        if (cc < c) run += chunk_sum[cc][i];
-        total += chunk_sum[cc][i];
-    }
-    if (b < n_buckets) {
-#pragma unroll 8
-        for (int64_t t = t_lo; t < t_hi; ++t) {
-            const int32_t v = counts[t * n_buckets + b];
-            counts[t * n_buckets + b] = run;
-            run += v;
-        }
-        if (c == 0) tot[b] = total;
-    }
-    if (blockIdx.x == 0) {
-        int bad = 0;
-        for (int64_t t = threadIdx.x; t < tiles; t += blockDim.x) bad |= tile_bad[t];
-        bad = __syncthreads_or(bad);
-        if (threadIdx.x == 0) *flag = bad ? 1 : 0;
-    }
-}
-
-// Per tile: pairs[pos] = (dst, e) grouped by bucket; dst32[e].  LDS: the
-// running offsets of the kParts parts, kParts x NB entries.  Part w of the
-// tile starts, for bucket b, at
-//   start[b] + (edges of b in earlier tiles) + (edges of b in parts < w).
-__global__ __launch_bounds__(kThreads) void csr_bucket_place_kernel(
-    const int64_t* __restrict__ dst, int64_t n_edges, int64_t n_nodes, int64_t tile_edges,
-    int sb, int64_t n_buckets, int bucket_bits, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ tot, int2* __restrict__ pairs, int32_t* __restrict__ dst32,
-    int32_t* __restrict__ starts) {
-    extern __shared__ int32_t lds[];   // [0, NB): base; [NB, (1 + kParts) NB): parts
-    int32_t* base = lds;
-    int32_t* run_all = lds + n_buckets;
-    const int64_t t = blockIdx.x;
-    const int64_t e0 = t * tile_edges;
-    const int64_t e1 = e0 + tile_edges < n_edges ? e0 + tile_edges : n_edges;
-    const int64_t part = (e1 - e0 + kParts - 1) / kParts;
-    const int wave = threadIdx.x >> 6;
+// One 64-edge step of a stable placement: the lanes with ok set and equal
+// key (bits wide) are ranked in lane order and take consecutive positions from
+// run[key], which the step advances.  Returns the lane's position (unused when
+// !ok).  run is this wavefront's own LDS table, or with kAtomic a table in
+// global memory that only this wavefront updates.
+template <bool kAtomic>
+__device__ __attribute__((always_inline)) inline int64_t place_step(bool ok, int32_t key, int bits,
+                                                                    int32_t* run) {
     const int lane = threadIdx.x & 63;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const uint64_t same = match_key(ok, key, bits);
+    const int rank = __popcll(same & below);
+    const int cnt = __popcll(same);
+    const int leader = ok ? __ffsll((unsigned long long)same) - 1 : lane;
+    int32_t o = 0;
+    if (!kAtomic) wave_lds_sync();   // the previous step's leaders wrote run[] entries read here
+    if (ok && rank == 0) {
+        if (kAtomic) {
+            o = atomicAdd(&run[key], cnt);   // returns the running offset
+        } else {
+            o = run[key];
+            run[key] = o + cnt;
+        }
+    }
+    o = __shfl(o, leader, 64);
+    return int64_t(o) + rank;
+}
+
+// ---- kernel 1: sort each chunk by bucket ------------------------------------
+
+// LDS: per-part bucket counts, then running offsets (kParts x NB), and the
+// chunk's bucket offsets (NB).  Part w of chunk c starts, for bucket b, at
+//   loff[c][b] + (edges of b in parts < w of c).
+__global__ __launch_bounds__(kThreads) void csr_chunk_sort_kernel(
+    const int64_t* __restrict__ dst, int64_t n_edges, int64_t n_nodes, int64_t chunk_edges,
+    int sb, int64_t n_buckets, int bucket_bits, int32_t* __restrict__ dst32,
+    int32_t* __restrict__ loff, int32_t* __restrict__ chunk_bad, int2* __restrict__ pairs) {
+    extern __shared__ int32_t lds[];
+    int32_t* run_all = lds;
+    int32_t* boff = lds + kParts * n_buckets;
+    const int64_t c = blockIdx.x;
+    const int64_t e0 = c * chunk_edges;
+    const int64_t e1 = e0 + chunk_edges < n_edges ? e0 + chunk_edges : n_edges;
+    const int64_t part = (e1 - e0 + kParts - 1) / kParts;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
     const int64_t p0 = e0 + wave * part < e1 ? e0 + wave * part : e1;
     const int64_t p1 = p0 + part < e1 ? p0 + part : e1;
 
-    // this part's first keys are requested before anything else
-    const bool single = p1 - p0 <= 64 * kAhead;
-    int64_t keys[kAhead];
+    // keys of edges [at, at + 64 * kAhead) of this part (-1: none or out of range)
+    int32_t keys[kAhead];
+    int bad = 0;
+    auto load = [&](int64_t at, bool write) {
+        int64_t d[kAhead];
 #pragma unroll
-    for (int j = 0; j < kAhead; ++j) {
-        const int64_t e = p0 + j * 64 + lane;
-        keys[j] = e < p1 ? dst[e] : -1;
-    }
-    // bucket starts (tile 0 publishes them for the node level), plus this
-    // tile's offsets within each bucket
-    lds_load(base, tot, n_buckets);
-    for (int64_t i = threadIdx.x; i < kParts * n_buckets; i += kThreads) run_all[i] = 0;
-    __syncthreads();
-    const int32_t total = block_exclusive_scan_lds(base, n_buckets);
-    if (t == 0) {
-        for (int64_t i = threadIdx.x; i < n_buckets; i += kThreads) starts[i] = base[i];
-        if (threadIdx.x == 0) starts[n_buckets] = total;
-    }
-    {
-        const int32_t* row = counts + t * n_buckets;
-        constexpr int U = 16;
-        for (int64_t b0 = 0; b0 < n_buckets; b0 += int64_t(kThreads) * U) {
-            int32_t v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t i = b0 + int64_t(u) * kThreads + threadIdx.x;
-                v[u] = i < n_buckets ? row[i] : 0;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t i = b0 + int64_t(u) * kThreads + threadIdx.x;
-                if (i < n_buckets) base[i] += v[u];
-            }
-        }
-    }
-    // per-part histograms; a part of at most kAhead steps keeps its keys in
-    // registers for the placement pass
-    for (int64_t chunk = p0; chunk < p1; chunk += 64 * kAhead) {
-        if (chunk != p0) {
-#pragma unroll
-            for (int j = 0; j < kAhead; ++j) {
-                const int64_t e = chunk + j * 64 + lane;
-                keys[j] = e < p1 ? dst[e] : -1;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kAhead; ++j)
-            if (keys[j] >= 0 && keys[j] < n_nodes)
-                atomicAdd(&run_all[wave * n_buckets + (keys[j] >> sb)], 1);
-    }
-    __syncthreads();
-    for (int64_t b = threadIdx.x; b < n_buckets; b += kThreads) {
-        int32_t o = base[b];
-#pragma unroll
-        for (int w = 0; w < kParts; ++w) {
-            const int32_t c = run_all[w * n_buckets + b];
-            run_all[w * n_buckets + b] = o;
-            o += c;
-        }
-    }
-    __syncthreads();
-
-    int32_t* run = run_all + wave * n_buckets;
-    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    for (int64_t chunk = p0; chunk < p1; chunk += 64 * kAhead) {
-        if (!single) {
-#pragma unroll
-            for (int j = 0; j < kAhead; ++j) {
-                const int64_t e = chunk + j * 64 + lane;
-                keys[j] = e < p1 ? dst[e] : -1;
-            }
+        for (int j = 0; j < kAhead; ++j) {
+            const int64_t e = at + j * 64 + lane;
+            d[j] = e < p1 ? dst[e] : -1;
         }
 #pragma unroll
         for (int j = 0; j < kAhead; ++j) {
-            if (chunk + j * 64 >= p1) break;           // uniform
-            const int64_t e = chunk + j * 64 + lane;
+            const int64_t e = at + j * 64 + lane;
             const bool in = e < p1;
-            const int64_t key64 = keys[j];
-            const bool ok = in && key64 >= 0 && key64 < n_nodes;
-            const int32_t key = ok ? int32_t(key64) : 0;
-            if (in) dst32[e] = ok ? key : -1;
-            const int32_t bucket = key >> sb;
-            const uint64_t same = match_key(ok, bucket, bucket_bits);
-            const int rank = __popcll(same & below);
-            const int cnt = __popcll(same);
-            const int leader = ok ? __ffsll((unsigned long long)same) - 1 : lane;
-            int32_t o = 0;
-            wave_lds_sync();   // the previous step's leaders wrote run[] entries read here
-            if (ok && rank == 0) {
-                o = run[bucket];
-                run[bucket] = o + cnt;
+            const bool ok = in && d[j] >= 0 && d[j] < n_nodes;
+            keys[j] = ok ? int32_t(d[j]) : -1;
+            if (write && in) {
+                dst32[e] = keys[j];
+                bad |= !ok;
             }
-            o = __shfl(o, leader, 64);
-            const int64_t pos = int64_t(o) + rank;
-            if (ok && pos >= 0 && pos < n_edges) pairs[pos] = make_int2(key, int32_t(e));
+        }
+    };
+    const bool single = p1 - p0 <= 64 * kAhead;
+    load(p0, true);
+    for (int64_t i = tid; i < kParts * n_buckets; i += kThreads) run_all[i] = 0;
+    __syncthreads();
+    // per-part histograms
+    for (int64_t at = p0; at < p1; at += 64 * kAhead) {
+        if (at != p0) load(at, true);
+#pragma unroll
+        for (int j = 0; j < kAhead; ++j)
+            if (keys[j] >= 0) atomicAdd(&run_all[wave * n_buckets + (keys[j] >> sb)], 1);
+    }
+    __syncthreads();
+    for (int64_t b = tid; b < n_buckets; b += kThreads) {
+        int32_t s = 0;
+#pragma unroll
+        for (int w = 0; w < kParts; ++w) s += run_all[w * n_buckets + b];
+        boff[b] = s;
+    }
+    __syncthreads();
+    const int32_t valid = block_exclusive_scan_lds<kThreads>(boff, n_buckets);
+    int32_t* row = loff + c * (n_buckets + 1);
+    for (int64_t b = tid; b < n_buckets; b += kThreads) {
+        int32_t o = boff[b];
+        row[b] = o;
+#pragma unroll
+        for (int w = 0; w < kParts; ++w) {
+            const int32_t n = run_all[w * n_buckets + b];
+            run_all[w * n_buckets + b] = o;
+            o += n;
+        }
+    }
+    if (tid == 0) row[n_buckets] = valid;
+    bad = __syncthreads_or(bad);
+    if (tid == 0) chunk_bad[c] = bad;
+
+    int32_t* run = run_all + wave * n_buckets;
+    int2* out = pairs + e0;
+    const int64_t len = e1 - e0;
+    for (int64_t at = p0; at < p1; at += 64 * kAhead) {
+        if (!single) load(at, false);
+#pragma unroll
+        for (int j = 0; j < kAhead; ++j) {
+            if (at + j * 64 >= p1) break;              // uniform
+            const int64_t e = at + j * 64 + lane;
+            const bool ok = keys[j] >= 0;
+            const int32_t key = ok ? keys[j] : 0;
+            const int64_t pos = place_step<false>(ok, key >> sb, bucket_bits, run);
+            if (ok && pos >= 0 && pos < len) out[pos] = make_int2(key, int32_t(e));
         }
     }
 }
 
-// ---- level 2: nodes within a bucket -------------------------------------------
+// ---- kernel 2: place each bucket's edges by node ----------------------------
 
-// One workgroup per bucket b (nodes [b*BN, min(N, (b+1)*BN))).  Its pairs are
-// the contiguous run [starts[b], starts[b + 1]) in increasing edge id.
-// LDS path (BN <= kNodeLdsMax): per-part histograms and running offsets in LDS,
-// kParts wavefronts.  Global path: one wavefront, running offsets in `scratch`
-// (the bucket's own BN entries of an N-entry workspace array).
-template <bool kLds>
-__global__ __launch_bounds__(kThreads) void csr_node_place_kernel(
-    const int2* __restrict__ pairs, int64_t n_edges, int64_t n_nodes, int sb, int64_t n_buckets,
-    const int32_t* __restrict__ starts, int32_t* __restrict__ rowptr, int32_t* __restrict__ perm,
-    int32_t* __restrict__ scratch) {
-    extern __shared__ int32_t lds[];   // kLds: [0, BN): node offsets; then kParts x BN
-    const int64_t b = blockIdx.x;
+// The bucket's edge sequence (increasing edge id) is the concatenation over
+// chunks of their runs.  runpre[c] = first sequence index of chunk c's run
+// (runpre[W] = the bucket's size), runoff[c] = the run's offset in its chunk.
+struct BucketRuns {
+    const int32_t* runpre;
+    const int32_t* runoff;
+    int64_t chunks;
+    int64_t chunk_edges;
+    const int2* pairs;
+
+    // pair at sequence index i (0 <= i < runpre[W])
+    __device__ __attribute__((always_inline)) int2 at(int64_t i) const {
+        int64_t lo = 0, hi = chunks - 1;      // largest c with runpre[c] <= i
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if (runpre[mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        return pairs[lo * chunk_edges + runoff[lo] + (i - runpre[lo])];
+    }
+};
+
+// Collects the bucket's runs into LDS (runpre, runoff: W + 1 and W entries)
+// and returns the bucket's first CSR position; runpre[W] holds its size.
+template <int TH>
+__device__ __attribute__((always_inline)) inline int64_t bucket_runs(
+    const int32_t* __restrict__ loff, int64_t chunks, int64_t n_buckets, int64_t b,
+    int32_t* runpre, int32_t* runoff) {
+    int64_t before = 0;
+    for (int64_t c = threadIdx.x; c < chunks; c += TH) {
+        const int32_t* row = loff + c * (n_buckets + 1);
+        const int32_t lo = row[b], hi = row[b + 1];
+        runoff[c] = lo;
+        runpre[c] = hi - lo;
+        before += lo;
+    }
+    const int64_t start = block_sum<TH>(before);   // (its barriers order the LDS writes)
+    const int32_t size = block_exclusive_scan_lds<TH>(runpre, chunks);
+    if (threadIdx.x == 0) runpre[chunks] = size;
+    __syncthreads();
+    return start;
+}
+
+// Folds the per-chunk out-of-range bits into the flag (one workgroup).
+template <int TH>
+__device__ __attribute__((always_inline)) inline void fold_flag(
+    const int32_t* __restrict__ chunk_bad, int64_t chunks, int32_t* __restrict__ flag) {
+    int bad = 0;
+    for (int64_t c = threadIdx.x; c < chunks; c += TH) bad |= chunk_bad[c];
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) *flag = bad ? 1 : 0;
+}
+
+// LDS path (BN <= kNodeLdsMax).  LDS: runpre (W + 1), runoff (W), per-part
+// node counts then running offsets (kParts x BN), node offsets (BN).
+__global__ __launch_bounds__(kThreads) void csr_bucket_place_kernel(
+    const int2* __restrict__ pairs, const int32_t* __restrict__ loff,
+    const int32_t* __restrict__ chunk_bad, int64_t chunks, int64_t chunk_edges, int64_t n_edges,
+    int64_t n_nodes, int sb, int64_t n_buckets, int32_t* __restrict__ flag,
+    int32_t* __restrict__ rowptr, int32_t* __restrict__ perm) {
+    extern __shared__ int32_t lds[];
     const int64_t bn = int64_t(1) << sb;
+    int32_t* runpre = lds;
+    int32_t* runoff = lds + chunks + 1;
+    int32_t* run_all = runoff + chunks;
+    int32_t* noff = run_all + kParts * bn;
+    const int64_t b = blockIdx.x;
     const int64_t n0 = b * bn;
     const int64_t nn = n0 + bn < n_nodes ? bn : n_nodes - n0;   // nodes in this bucket
-    const int32_t s0 = starts[b];                                 // the bucket's run of pairs
-    const int64_t r0 = s0, r1 = starts[b + 1];
-    constexpr int PW = kLds ? kParts : 1;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int64_t part = (r1 - r0 + PW - 1) / PW;
-    const int64_t p0 = r0 + wave * part < r1 ? r0 + wave * part : r1;
-    const int64_t p1 = p0 + part < r1 ? p0 + part : r1;
-    int32_t* node_off = kLds ? lds : scratch + n0;
-    int32_t* run_all = lds + bn;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    if (b == 0) fold_flag<kThreads>(chunk_bad, chunks, flag);
+    for (int64_t i = tid; i < kParts * bn; i += kThreads) run_all[i] = 0;
+    const int64_t start = bucket_runs<kThreads>(loff, chunks, n_buckets, b, runpre, runoff);
+    const BucketRuns seq{runpre, runoff, chunks, chunk_edges, pairs};
+    const int64_t size = runpre[chunks];
+    const int64_t part = (size + kParts - 1) / kParts;
+    const int64_t p0 = wave * part < size ? wave * part : size;
+    const int64_t p1 = p0 + part < size ? p0 + part : size;
 
-    // per-part histograms of the local node ids
-    if (kLds) {
-        for (int64_t i = threadIdx.x; i < (1 + PW) * bn; i += kThreads) lds[i] = 0;
-    } else {
-        for (int64_t i = threadIdx.x; i < nn; i += kThreads) node_off[i] = 0;
-    }
-    __syncthreads();
-    // a part of at most kAhead2 steps keeps its pairs in registers for the
-    // placement pass
-    constexpr int kAhead2 = 16;
-    const bool single = p1 - p0 <= 64 * kAhead2;
-    int2 pr[kAhead2];
-    if (wave < PW) {
-        for (int64_t chunk = p0; chunk < p1; chunk += 64 * kAhead2) {
+    const bool single = p1 - p0 <= 64 * kAhead;
+    int2 pr[kAhead];
+    auto load = [&](int64_t at) {
 #pragma unroll
-            for (int j = 0; j < kAhead2; ++j) {
-                const int64_t k = chunk + j * 64 + lane;
-                pr[j] = k < p1 ? pairs[k] : make_int2(-1, -1);
-            }
+        for (int j = 0; j < kAhead; ++j) {
+            const int64_t i = at + j * 64 + lane;
+            pr[j] = i < p1 ? seq.at(i) : make_int2(-1, -1);
+        }
+    };
+    for (int64_t at = p0; at < p1; at += 64 * kAhead) {
+        load(at);
 #pragma unroll
-            for (int j = 0; j < kAhead2; ++j) {
-                const int64_t loc = int64_t(pr[j].x) - n0;
-                if (pr[j].x >= 0 && loc >= 0 && loc < nn) {
-                    if (kLds)
-                        atomicAdd(&run_all[wave * bn + loc], 1);
-                    else
-                        atomicAdd(&node_off[loc], 1);
-                }
-            }
+        for (int j = 0; j < kAhead; ++j) {
+            const int64_t loc = int64_t(pr[j].x) - n0;
+            if (pr[j].x >= 0 && loc >= 0 && loc < nn) atomicAdd(&run_all[wave * bn + loc], 1);
         }
     }
     __syncthreads();
-    // node offsets: exclusive scan over the bucket's nodes of their totals
-    if (kLds) {
-        for (int64_t i = threadIdx.x; i < nn; i += kThreads) {
-            int32_t s = 0;
+    for (int64_t n = tid; n < nn; n += kThreads) {
+        int32_t s = 0;
 #pragma unroll
-            for (int w = 0; w < PW; ++w) s += run_all[w * bn + i];
-            node_off[i] = s;
-        }
-        __syncthreads();
-        block_exclusive_scan_lds(node_off, nn);
-    } else if (threadIdx.x < 64) {
-        int32_t carry = 0;
-        for (int64_t base = 0; base < nn; base += 64) {
-            const int64_t i = base + lane;
-            const int32_t x = i < nn ? node_off[i] : 0;
-            const int32_t incl = wave_inclusive_scan(x);
-            if (i < nn) node_off[i] = carry + incl - x;
-            carry += __shfl(incl, 63, 64);
-        }
+        for (int w = 0; w < kParts; ++w) s += run_all[w * bn + n];
+        noff[n] = s;
     }
     __syncthreads();
-    for (int64_t i = threadIdx.x; i < nn; i += kThreads) rowptr[n0 + i] = s0 + node_off[i];
-    if (b == n_buckets - 1 && threadIdx.x == 0) rowptr[n_nodes] = int32_t(r1);
-    if (kLds) {
-        for (int64_t i = threadIdx.x; i < nn; i += kThreads) {
-            int32_t o = s0 + node_off[i];
+    block_exclusive_scan_lds<kThreads>(noff, nn);
+    for (int64_t n = tid; n < nn; n += kThreads) {
+        int32_t o = int32_t(start) + noff[n];
+        rowptr[n0 + n] = o;
 #pragma unroll
-            for (int w = 0; w < PW; ++w) {
-                const int32_t c = run_all[w * bn + i];
-                run_all[w * bn + i] = o;
-                o += c;
-            }
+        for (int w = 0; w < kParts; ++w) {
+            const int32_t k = run_all[w * bn + n];
+            run_all[w * bn + n] = o;
+            o += k;
         }
-    } else {
-        for (int64_t i = threadIdx.x; i < nn; i += kThreads) node_off[i] += s0;
     }
+    if (b == n_buckets - 1 && tid == 0) rowptr[n_nodes] = int32_t(start + size);
     __syncthreads();
-    if (wave >= PW) return;
 
-    int32_t* run = kLds ? run_all + wave * bn : node_off;
-    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    for (int64_t chunk = p0; chunk < p1; chunk += 64 * kAhead2) {
-        if (!single) {
+    int32_t* run = run_all + wave * bn;
+    for (int64_t at = p0; at < p1; at += 64 * kAhead) {
+        if (!single) load(at);
 #pragma unroll
-            for (int j = 0; j < kAhead2; ++j) {
-                const int64_t k = chunk + j * 64 + lane;
-                pr[j] = k < p1 ? pairs[k] : make_int2(-1, -1);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kAhead2; ++j) {
-            if (chunk + j * 64 >= p1) break;           // uniform
+        for (int j = 0; j < kAhead; ++j) {
+            if (at + j * 64 >= p1) break;              // uniform
             const int64_t loc64 = int64_t(pr[j].x) - n0;
             const bool ok = pr[j].x >= 0 && loc64 >= 0 && loc64 < nn;
-            const int32_t loc = ok ? int32_t(loc64) : 0;
-            const uint64_t same = match_key(ok, loc, sb);
-            const int rank = __popcll(same & below);
-            const int cnt = __popcll(same);
-            const int leader = ok ? __ffsll((unsigned long long)same) - 1 : lane;
-            int32_t o = 0;
-            if (kLds) wave_lds_sync();   // the previous step's leaders wrote run[] entries read here
-            if (ok && rank == 0) {
-                if (kLds) {
-                    o = run[loc];
-                    run[loc] = o + cnt;
-                } else {
-                    o = atomicAdd(&run[loc], cnt);   // returns the running offset
-                }
-            }
-            o = __shfl(o, leader, 64);
-            const int64_t pos = int64_t(o) + rank;
+            const int64_t pos = place_step<false>(ok, ok ? int32_t(loc64) : 0, sb, run);
             if (ok && pos >= 0 && pos < n_edges) perm[pos] = pr[j].y;
         }
+    }
+}
+
+// Global path (BN > kNodeLdsMax): node counts and running offsets in
+// `scratch` (the bucket's own BN entries of an N-entry workspace array); all
+// wavefronts count, wavefront 0 scans and places (in sequence order, so the
+// placement is stable).  LDS: runpre (W + 1), runoff (W).
+__global__ __launch_bounds__(kGlobalThreads) void csr_bucket_place_global_kernel(
+    const int2* __restrict__ pairs, const int32_t* __restrict__ loff,
+    const int32_t* __restrict__ chunk_bad, int64_t chunks, int64_t chunk_edges, int64_t n_edges,
+    int64_t n_nodes, int sb, int64_t n_buckets, int32_t* __restrict__ flag,
+    int32_t* __restrict__ rowptr, int32_t* __restrict__ perm, int32_t* __restrict__ scratch) {
+    extern __shared__ int32_t lds[];
+    const int64_t bn = int64_t(1) << sb;
+    int32_t* runpre = lds;
+    int32_t* runoff = lds + chunks + 1;
+    const int64_t b = blockIdx.x;
+    const int64_t n0 = b * bn;
+    const int64_t nn = n0 + bn < n_nodes ? bn : n_nodes - n0;
+    int32_t* node_off = scratch + n0;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    if (b == 0) fold_flag<kGlobalThreads>(chunk_bad, chunks, flag);
+    for (int64_t n = tid; n < nn; n += kGlobalThreads) node_off[n] = 0;
+    const int64_t start = bucket_runs<kGlobalThreads>(loff, chunks, n_buckets, b, runpre,
+                                                      runoff);
+    const BucketRuns seq{runpre, runoff, chunks, chunk_edges, pairs};
+    const int64_t size = runpre[chunks];
+    for (int64_t i = tid; i < size; i += kGlobalThreads) {
+        const int2 p = seq.at(i);
+        const int64_t loc = int64_t(p.x) - n0;
+        if (p.x >= 0 && loc >= 0 && loc < nn) atomicAdd(&node_off[loc], 1);
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid < 64) {
+        int32_t carry = int32_t(start);
+        for (int64_t base = 0; base < nn; base += 64) {
+            const int64_t n = base + lane;
+            const int32_t x = n < nn ? node_off[n] : 0;
+            const int32_t incl = wave_inclusive_scan(x);
+            if (n < nn) {
+                node_off[n] = carry + incl - x;
+                rowptr[n0 + n] = carry + incl - x;
+            }
+            carry += __shfl(incl, 63, 64);
+        }
+        if (b == n_buckets - 1 && lane == 0) rowptr[n_nodes] = int32_t(start + size);
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid >= 64) return;
+    for (int64_t base = 0; base < size; base += 64) {
+        const int64_t i = base + lane;
+        const int2 p = i < size ? seq.at(i) : make_int2(-1, -1);
+        const int64_t loc64 = int64_t(p.x) - n0;
+        const bool ok = p.x >= 0 && loc64 >= 0 && loc64 < nn;
+        const int64_t pos = place_step<true>(ok, ok ? int32_t(loc64) : 0, sb, node_off);
+        if (ok && pos >= 0 && pos < n_edges) perm[pos] = p.y;
     }
 }
 
@@ -501,27 +484,27 @@ CsrPlan plan_csr(int64_t n_edges, int64_t n_nodes) {
     CsrPlan p{};
     int node_bits = 0;
     while (node_bits < 62 && (int64_t(1) << node_bits) < n_nodes) ++node_bits;
-    p.bucket_shift = node_bits - kBucketsMaxBits > kBucketMinBits ? node_bits - kBucketsMaxBits
-                                                                   : kBucketMinBits;
-    p.buckets = (n_nodes + (int64_t(1) << p.bucket_shift) - 1) >> p.bucket_shift;
+    // at most 256 buckets while a bucket's nodes fit the LDS tables, else up
+    // to 1024 (then, past 2^19 nodes, node tables in global memory)
+    int sb = node_bits > kBucketBitsSmall ? node_bits - kBucketBitsSmall : 0;
+    if ((int64_t(1) << sb) > kNodeLdsMax)
+        sb = node_bits > kBucketBitsMax ? node_bits - kBucketBitsMax : 0;
+    p.bucket_shift = sb;
+    p.buckets = (n_nodes + (int64_t(1) << sb) - 1) >> sb;
     p.bucket_bits = 0;
     while ((int64_t(1) << p.bucket_bits) < p.buckets) ++p.bucket_bits;
-    p.node_lds = (int64_t(1) << p.bucket_shift) <= kNodeLdsMax;
-    // tiles: as many 1024-edge tiles as the count matrix budget allows
-    int64_t max_tiles = kCountBudget / p.buckets;
-    if (max_tiles > kTilesMax) max_tiles = kTilesMax;
-    if (max_tiles < 1) max_tiles = 1;
-    int64_t tile_edges = (n_edges + max_tiles - 1) / max_tiles;
-    if (tile_edges < kTileEdgesMin) tile_edges = kTileEdgesMin;
-    p.tile_edges = tile_edges;
-    p.tiles = n_edges > 0 ? (n_edges + tile_edges - 1) / tile_edges : 1;
+    p.node_lds = (int64_t(1) << sb) <= kNodeLdsMax;
+    int64_t chunk = (n_edges + kChunksMax - 1) / kChunksMax;
+    const int64_t chunk_min = n_edges >= kChunkLargeFrom ? kChunkEdgesLarge : kChunkEdgesSmall;
+    if (chunk < chunk_min) chunk = chunk_min;
+    p.chunk_edges = chunk;
+    p.chunks = n_edges > 0 ? (n_edges + chunk - 1) / chunk : 1;
     auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
     p.off_flag = 0;
-    p.off_tile_bad = 256;
-    p.off_counts = align(p.off_tile_bad + size_t(p.tiles) * sizeof(int32_t));
-    p.off_tot = align(p.off_counts + size_t(p.tiles) * size_t(p.buckets) * sizeof(int32_t));
-    p.off_starts = align(p.off_tot + size_t(p.buckets) * sizeof(int32_t));
-    p.off_pairs = align(p.off_starts + size_t(p.buckets + 1) * sizeof(int32_t));
+    p.off_chunk_bad = 256;
+    p.off_loff = align(p.off_chunk_bad + size_t(p.chunks) * sizeof(int32_t));
+    p.off_pairs =
+        align(p.off_loff + size_t(p.chunks) * size_t(p.buckets + 1) * sizeof(int32_t));
     p.off_scratch = align(p.off_pairs + size_t(n_edges > 0 ? n_edges : 1) * sizeof(int2));
     p.bytes = align(p.off_scratch + (p.node_lds ? size_t(0) : size_t(n_nodes) * sizeof(int32_t)));
     return p;
@@ -532,39 +515,30 @@ hipError_t launch_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int3
                       int32_t* flag, hipStream_t stream) {
     char* ws = static_cast<char*>(workspace);
     if (!flag) flag = reinterpret_cast<int32_t*>(ws + plan.off_flag);
-    int32_t* tile_bad = reinterpret_cast<int32_t*>(ws + plan.off_tile_bad);
-    int32_t* counts = reinterpret_cast<int32_t*>(ws + plan.off_counts);
-    int32_t* tot = reinterpret_cast<int32_t*>(ws + plan.off_tot);
-    int32_t* starts = reinterpret_cast<int32_t*>(ws + plan.off_starts);
+    int32_t* chunk_bad = reinterpret_cast<int32_t*>(ws + plan.off_chunk_bad);
+    int32_t* loff = reinterpret_cast<int32_t*>(ws + plan.off_loff);
     int2* pairs = reinterpret_cast<int2*>(ws + plan.off_pairs);
     int32_t* scratch = reinterpret_cast<int32_t*>(ws + plan.off_scratch);
     const int sb = plan.bucket_shift;
     const int64_t nb = plan.buckets;
+    const int64_t W = plan.chunks;
     hipError_t err;
-    csr_bucket_count_kernel<<<unsigned(plan.tiles), kThreads, size_t(nb) * sizeof(int32_t),
-                              stream>>>(dst, n_edges, n_nodes, plan.tile_edges, sb, nb, counts,
-                                        tile_bad);
+    csr_chunk_sort_kernel<<<unsigned(W), kThreads,
+                            size_t(kParts + 1) * size_t(nb) * sizeof(int32_t), stream>>>(
+        dst, n_edges, n_nodes, plan.chunk_edges, sb, nb, plan.bucket_bits, dst32, loff, chunk_bad,
+        pairs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (plan.tiles <= kColFewTiles)
-        csr_bucket_scan_kernel<4><<<grid_for(nb, 4, int64_t(1) << 30), 4 * kColChunks, 0,
-                                    stream>>>(counts, plan.tiles, nb, tot, tile_bad, flag);
-    else
-        csr_bucket_scan_kernel<16><<<grid_for(nb, 16, int64_t(1) << 30), 16 * kColChunks, 0,
-                                     stream>>>(counts, plan.tiles, nb, tot, tile_bad, flag);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    csr_bucket_place_kernel<<<unsigned(plan.tiles), kThreads,
-                              size_t(1 + kParts) * size_t(nb) * sizeof(int32_t), stream>>>(
-        dst, n_edges, n_nodes, plan.tile_edges, sb, nb, plan.bucket_bits, counts, tot, pairs,
-        dst32, starts);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const size_t runs_lds = size_t(2 * W + 1) * sizeof(int32_t);
     const int64_t bn = int64_t(1) << sb;
     if (plan.node_lds)
-        csr_node_place_kernel<true><<<unsigned(nb), kThreads,
-                                      size_t(1 + kParts) * size_t(bn) * sizeof(int32_t), stream>>>(
-            pairs, n_edges, n_nodes, sb, nb, starts, rowptr, perm, scratch);
+        csr_bucket_place_kernel<<<unsigned(nb), kThreads,
+                                  runs_lds + size_t(kParts + 1) * size_t(bn) * sizeof(int32_t),
+                                  stream>>>(pairs, loff, chunk_bad, W, plan.chunk_edges, n_edges,
+                                            n_nodes, sb, nb, flag, rowptr, perm);
     else
-        csr_node_place_kernel<false><<<unsigned(nb), kThreads, 0, stream>>>(
-            pairs, n_edges, n_nodes, sb, nb, starts, rowptr, perm, scratch);
+        csr_bucket_place_global_kernel<<<unsigned(nb), kGlobalThreads, runs_lds, stream>>>(
+            pairs, loff, chunk_bad, W, plan.chunk_edges, n_edges, n_nodes, sb, nb, flag, rowptr,
+            perm, scratch);
     return hipGetLastError();
 }
 

@@ -113,9 +113,9 @@ int zs_build_csr(const int64_t *dst, int64_t n_edges, int64_t n_nodes,
  *       device.
  *
  * Returns ZS_ERR_SCRATCH, before any device work, when
- * zs_csr_workspace_bytes(n_edges, n_nodes) > ZS_NOALLOC_SCRATCH_BYTES (at
- * 4096 nodes about 3.3 million edges fit; at 16384 nodes the 2.6 million-edge
- * frame needs 27.9 MiB).  Nothing in the buffer has to start at zero: every
+ * zs_csr_workspace_bytes(n_edges, n_nodes) > ZS_NOALLOC_SCRATCH_BYTES (about
+ * 4 million edges fit at 1000 to 16384 nodes; the 2.6 million-edge,
+ * 16384-node frame needs 20.5 MiB).  Nothing in the buffer has to start at zero: every
  * entry a build reads was written earlier in the same build.  All calls on
  * one device share its buffer, so calls whose work overlaps on that device
  * (other streams, other threads) race: serialize them.

@@ -66,8 +66,7 @@ def test_noalloc_matches_workspace_build_twice(dev):
 
 
 def test_noalloc_large_frame_then_tiny(dev):
-    """The 16384-node frame (27.9 MiB of scratch, near the limit), then the
-    64-node frame."""
+    """The 16384-node frame (20.5 MiB of scratch), then the 64-node frame."""
     for name in ("large", "tiny"):
         w = synthetic.WORKLOADS[name]
         N, E = w.n_nodes, w.n_edges
