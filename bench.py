@@ -131,12 +131,12 @@ def _kernel_short_name(name: str) -> str:
     return name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
 
 
-def write_traffic(fetch_csv: str, write_csv: str) -> dict:
+def write_traffic(fetch_csv: str, write_csv: str, out_path: str | None = None) -> dict:
     """Per-kernel HBM bytes per launch from two rocprofv3 --pmc runs of
     ``bench.py --calibrate-copy`` (FETCH_SIZE, then WRITE_SIZE; KiB per
     dispatch), each scaled by what the same counter reads for the plain
     256 MiB device copy of the same run.  Writes profiles/traffic_headline.json
-    and returns it."""
+    (or out_path) and returns it."""
     import csv
     import collections
 
@@ -175,7 +175,7 @@ def write_traffic(fetch_csv: str, write_csv: str) -> dict:
            "calibration_copy_bytes": COPY_CALIBRATION_BYTES,
            "calibration_fetch_kib_raw": fcopies, "calibration_write_kib_raw": wcopies,
            "kernels": {k: (list(v.values())[0] if len(v) == 1 else v) for k, v in kernels.items()}}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(out_path or TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     return out
 
@@ -538,15 +538,20 @@ def main() -> int:
     ap.add_argument("--inputs", default="contiguous", choices=["contiguous", "views"],
                     help="views: coupling read in place from a packed (E, 46) Wigner band and "
                          "radial features sliced from an (E, 5, C) tensor (strided entry points)")
-    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="summarize two rocprofv3 --pmc counter_collection.csv files "
-                         "(FETCH_SIZE, WRITE_SIZE) into profiles/traffic_headline.json and exit")
+    ap.add_argument("--write-traffic", nargs="+", metavar="CSV",
+                    help="FETCH_CSV WRITE_CSV [OUT_JSON]: summarize two rocprofv3 --pmc "
+                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) into "
+                         "profiles/traffic_headline.json (or OUT_JSON) and exit")
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="print the mean per dispatch of every counter in these rocprofv3 --pmc "
                          "counter_collection.csv files, per zs:: kernel, and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 256 MiB device copy three times "
                          "(reference kernel for scaling rocprofv3 byte counters)")
+    ap.add_argument("--flush", choices=["none", "read", "fill"], default="none",
+                    help="empty the caches before every warmup and timed step (read: sum a "
+                         "512 MiB buffer; fill: overwrite it), e.g. for counter runs of cold "
+                         "launches; the line's value is then the cold figure")
     ap.add_argument("--processes", type=int, default=3,
                     help="fresh-process protocol in this many child processes (0: skip it)")
     ap.add_argument("--no-workloads", action="store_true",
@@ -555,6 +560,8 @@ def main() -> int:
     ap.add_argument("--protocol-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.write_traffic:
+        if len(args.write_traffic) not in (2, 3):
+            ap.error("--write-traffic takes FETCH_CSV WRITE_CSV [OUT_JSON]")
         print(json.dumps(write_traffic(*args.write_traffic), indent=1))
         return 0
     if args.summarize_counters:
@@ -602,10 +609,14 @@ def main() -> int:
     gc = torch.empty((E, 15), device=dev)
     gr = torch.empty((E, 3, C), device=dev)
 
+    step_flusher = Flusher(torch, dev) if args.flush != "none" else None
+
     def step(evs=None, split=False):
         """One step.  evs: [before build, before forward, between (split only),
         after backward]; the forward + backward time is the span of one event
         pair (an event between the two calls adds a few microseconds of its own)."""
+        if step_flusher is not None:
+            step_flusher(args.flush)
         if evs is not None:
             evs[0].record()
         zs.zs_build_csr(dst, N, workspace=ws, out=csr, bad_flag=flag)
@@ -677,7 +688,7 @@ def main() -> int:
         "config": {
             "workload": f"{w.name}: N={N} nodes, E={E} edges, C={C} channels, lmax=3, fp32",
             "n_nodes": N, "n_edges": E, "channels": C, "dst": w.dst_kind,
-            "inputs": args.inputs,
+            "inputs": args.inputs, "flush_before_step": args.flush,
         },
         "fwd_bwd_us": round(fb_us, 2),
         "fwd_us": round(fwd_us, 2),

@@ -16,7 +16,7 @@ struct CsrPlan {
     bool node_lds;        // per-bucket node tables fit in LDS
     size_t off_flag;      // int32 error flag
     size_t off_chunk_bad; // int32 [W] per-chunk out-of-range indicator
-    size_t off_loff;      // int32 [W][NB + 1] offset of each bucket's run in each chunk
+    size_t off_loff;      // int32 [NB + 1][W] offset of each bucket's run in each chunk
     size_t off_pairs;     // int2 [n_edges] (destination, edge), chunk-major, bucket runs
     size_t off_scratch;   // int32 [n_nodes] node offsets (only without node_lds)
     size_t bytes;         // total workspace bytes

@@ -17,17 +17,17 @@
 //                   per-part histograms give each part its offsets; lanes with
 //                   equal bucket ids are matched with ballots and ranked by
 //                   lane order) and writes the offset of every bucket's run in
-//                   the chunk, loff[c][b] (loff[c][NB] = the chunk's valid
-//                   edges).
+//                   the chunk, loff[b][c] (loff[NB][c] = the chunk's valid
+//                   edges; bucket-major, so a bucket's entries are contiguous).
 //   2. bucket_place one workgroup per bucket b: its edges, in increasing edge
-//                   id, are the runs [loff[c][b], loff[c][b + 1]) of chunks
+//                   id, are the runs [loff[b][c], loff[b + 1][c]) of chunks
 //                   c = 0, 1, ... in turn, and the bucket's first CSR position
-//                   is sum over c of loff[c][b] (every valid edge of a lower
+//                   is sum over c of loff[b][c] (every valid edge of a lower
 //                   bucket sits before b's run in its chunk).  The workgroup
 //                   gathers its runs, histograms the local node ids, writes
 //                   rowptr for its nodes and places perm stably the same way.
 //
-// Neither kernel reads more than a column pair of the W x NB offset table, so
+// Neither kernel reads more than two rows of the NB x W offset table, so
 // every workgroup is a few memory round trips deep.
 //
 // Every destination is range-checked; an out-of-range one is never used as an
@@ -173,7 +173,7 @@ __device__ __attribute__((always_inline)) inline int64_t place_step(bool ok, int
 
 // LDS: per-part bucket counts, then running offsets (kParts x NB), and the
 // chunk's bucket offsets (NB).  Part w of chunk c starts, for bucket b, at
-//   loff[c][b] + (edges of b in parts < w of c).
+//   loff[b][c] + (edges of b in parts < w of c).
 __global__ __launch_bounds__(kThreads) void csr_chunk_sort_kernel(
     const int64_t* __restrict__ dst, int64_t n_edges, int64_t n_nodes, int64_t chunk_edges,
     int sb, int64_t n_buckets, int bucket_bits, int32_t* __restrict__ dst32,
@@ -233,10 +233,10 @@ __global__ __launch_bounds__(kThreads) void csr_chunk_sort_kernel(
     }
     __syncthreads();
     const int32_t valid = block_exclusive_scan_lds<kThreads>(boff, n_buckets);
-    int32_t* row = loff + c * (n_buckets + 1);
+    const int64_t W = gridDim.x;   // chunks
     for (int64_t b = tid; b < n_buckets; b += kThreads) {
         int32_t o = boff[b];
-        row[b] = o;
+        loff[b * W + c] = o;
 #pragma unroll
         for (int w = 0; w < kParts; ++w) {
             const int32_t n = run_all[w * n_buckets + b];
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void csr_chunk_sort_kernel(
             o += n;
         }
     }
-    if (tid == 0) row[n_buckets] = valid;
+    if (tid == 0) loff[n_buckets * W + c] = valid;
     bad = __syncthreads_or(bad);
     if (tid == 0) chunk_bad[c] = bad;
 
@@ -296,8 +296,7 @@ __device__ __attribute__((always_inline)) inline int64_t bucket_runs(
     int32_t* runpre, int32_t* runoff) {
     int64_t before = 0;
     for (int64_t c = threadIdx.x; c < chunks; c += TH) {
-        const int32_t* row = loff + c * (n_buckets + 1);
-        const int32_t lo = row[b], hi = row[b + 1];
+        const int32_t lo = loff[b * chunks + c], hi = loff[(b + 1) * chunks + c];
         runoff[c] = lo;
         runpre[c] = hi - lo;
         before += lo;
