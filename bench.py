@@ -602,7 +602,8 @@ def main() -> int:
     g = torch.from_numpy(x["grad_out"]).to(dev)
     csr = zs.Csr(torch.empty(N + 1, dtype=torch.int32, device=dev),
                  torch.empty(E, dtype=torch.int32, device=dev),
-                 torch.empty(E, dtype=torch.int32, device=dev), N)
+                 torch.empty(E, dtype=torch.int32, device=dev), N,
+                 torch.empty(N, dtype=torch.int32, device=dev))
     ws = torch.empty(max(zs.zs_csr_workspace_bytes(E, N), 1), dtype=torch.uint8, device=dev)
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     out = torch.empty((N, 16, C), device=dev)

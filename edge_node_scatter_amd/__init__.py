@@ -7,7 +7,7 @@ is missing or no GPU is present, these functions raise.
 
 Functions carry the C ABI's names:
 
-* ``zs_build_csr(dst, n_nodes)`` -> ``Csr(rowptr, perm, dst32)``
+* ``zs_build_csr(dst, n_nodes)`` -> ``Csr(rowptr, perm, dst32, n_nodes, order)``
 * ``zs_forward(coupling, radial, csr)`` -> out (N, 16, C)
 * ``zs_backward(grad_out, coupling, radial, csr)`` -> (grad_coupling, grad_radial)
 * ``zs_forward_normalized(coupling, radial, env, csr)`` -> (y, out, norm)
@@ -64,20 +64,20 @@ def load() -> ctypes.CDLL:
         lib.zs_status_string.restype = ctypes.c_char_p
         lib.zs_csr_workspace_bytes.argtypes = [I64, I64]
         lib.zs_csr_workspace_bytes.restype = SZ
-        lib.zs_build_csr.argtypes = [P, I64, I64, P, P, P, P, SZ, P, P]
+        lib.zs_build_csr.argtypes = [P, I64, I64, P, P, P, P, P, SZ, P, P]
         lib.zs_build_csr.restype = INT
-        lib.zs_build_csr_noalloc.argtypes = [P, I64, I64, P, P, P, P, P]
+        lib.zs_build_csr_noalloc.argtypes = [P, I64, I64, P, P, P, P, P, P]
         lib.zs_build_csr_noalloc.restype = INT
-        lib.zs_forward.argtypes = [P, P, P, P, I64, I64, I64, P, P]
+        lib.zs_forward.argtypes = [P, P, P, P, P, I64, I64, I64, P, P]
         lib.zs_forward.restype = INT
         lib.zs_backward.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, P, P]
         lib.zs_backward.restype = INT
-        lib.zs_forward_strided.argtypes = [P, I64, P, I64, I64, P, P, I64, I64, I64, P, P]
+        lib.zs_forward_strided.argtypes = [P, I64, P, I64, I64, P, P, P, I64, I64, I64, P, P]
         lib.zs_forward_strided.restype = INT
         lib.zs_backward_strided.argtypes = [P, P, I64, P, I64, I64, P, P, P, I64, I64, I64, P, P,
                                             P]
         lib.zs_backward_strided.restype = INT
-        lib.zs_forward_normalized.argtypes = [P, P, P, P, P, I64, I64, I64, P, P, P, P]
+        lib.zs_forward_normalized.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, P, P, P]
         lib.zs_forward_normalized.restype = INT
         lib.zs_backward_normalized.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, P, P, P, P,
                                                P]
@@ -135,10 +135,13 @@ def _buffer(t: torch.Tensor, name: str, shape: tuple, dtype: torch.dtype,
 
 
 def _csr_buffers(csr: "Csr", n_edges: int, device: torch.device) -> None:
-    """The CSR arrays must hold N + 1 row offsets and E positions."""
+    """The CSR arrays must hold N + 1 row offsets, E positions and (when
+    present) N order entries."""
     _buffer(csr.rowptr, "csr.rowptr", (csr.n_nodes + 1,), torch.int32, device)
     _buffer(csr.perm, "csr.perm", (n_edges,), torch.int32, device)
     _buffer(csr.dst32, "csr.dst32", (n_edges,), torch.int32, device)
+    if csr.order is not None:
+        _buffer(csr.order, "csr.order", (csr.n_nodes,), torch.int32, device)
 
 
 def _edge_views(coupling: torch.Tensor, radial: torch.Tensor):
@@ -177,6 +180,7 @@ class Csr(NamedTuple):
     perm: torch.Tensor     # (E,) int32
     dst32: torch.Tensor    # (E,) int32
     n_nodes: int
+    order: torch.Tensor | None = None   # (N,) int32 node order for the forward, or None
 
 
 def zs_csr_workspace_bytes(n_edges: int, n_nodes: int) -> int:
@@ -184,13 +188,17 @@ def zs_csr_workspace_bytes(n_edges: int, n_nodes: int) -> int:
 
 
 def zs_build_csr(dst: torch.Tensor, n_nodes: int, workspace: torch.Tensor | None = None,
-                 out: Csr | None = None, bad_flag: torch.Tensor | None = None) -> Csr:
+                 out: Csr | None = None, bad_flag: torch.Tensor | None = None,
+                 order: bool = True) -> Csr:
     """Stable destination CSR of int64 ``dst``.
 
     Without ``bad_flag`` the call synchronizes the stream and raises ZsError
     (status ZS_ERR_INDEX) for a destination outside [0, n_nodes).  With a
     one-element int32 GPU tensor ``bad_flag`` it returns at once and the flag
     becomes nonzero, in stream order, if any destination was out of range.
+    A new Csr carries the node order (nodes by decreasing degree) unless
+    ``order`` is False; with ``out`` the order is written when out.order is
+    a tensor.
     """
     dst = _dev_tensor(dst, "dst", torch.int64)
     E = dst.numel()
@@ -198,7 +206,8 @@ def zs_build_csr(dst: torch.Tensor, n_nodes: int, workspace: torch.Tensor | None
     if out is None:
         out = Csr(torch.empty(n_nodes + 1, dtype=torch.int32, device=dev),
                   torch.empty(E, dtype=torch.int32, device=dev),
-                  torch.empty(E, dtype=torch.int32, device=dev), n_nodes)
+                  torch.empty(E, dtype=torch.int32, device=dev), n_nodes,
+                  torch.empty(n_nodes, dtype=torch.int32, device=dev) if order else None)
     elif out.n_nodes != n_nodes:
         raise ValueError(f"out.n_nodes is {out.n_nodes}, expected {n_nodes}")
     _csr_buffers(out, E, dev)
@@ -210,7 +219,7 @@ def zs_build_csr(dst: torch.Tensor, n_nodes: int, workspace: torch.Tensor | None
     if bad_flag is not None:
         _buffer(bad_flag, "bad_flag", (1,), torch.int32, dev)
     _check("zs_build_csr", load().zs_build_csr(
-        _ptr(dst), E, n_nodes, _ptr(out.rowptr), _ptr(out.perm), _ptr(out.dst32),
+        _ptr(dst), E, n_nodes, _ptr(out.rowptr), _ptr(out.perm), _ptr(out.dst32), _ptr(out.order),
         _ptr(workspace), workspace.numel(), _ptr(bad_flag), _stream()))
     return out
 
@@ -235,7 +244,7 @@ def zs_build_csr_noalloc(dst: torch.Tensor, n_nodes: int, out: Csr,
     if bad_flag is not None:
         _buffer(bad_flag, "bad_flag", (1,), torch.int32, dst.device)
     _check("zs_build_csr_noalloc", load().zs_build_csr_noalloc(
-        _ptr(dst), E, n_nodes, _ptr(out.rowptr), _ptr(out.perm), _ptr(out.dst32),
+        _ptr(dst), E, n_nodes, _ptr(out.rowptr), _ptr(out.perm), _ptr(out.dst32), _ptr(out.order),
         _ptr(bad_flag), _stream()))
     return out
 
@@ -258,11 +267,11 @@ def zs_forward(coupling: torch.Tensor, radial: torch.Tensor, csr: Csr,
         _buffer(out, "out", (csr.n_nodes, ROWS, C), torch.float32, dev)
     if coupling.is_contiguous() and radial.is_contiguous():
         status = load().zs_forward(_ptr(coupling), _ptr(radial), _ptr(csr.rowptr), _ptr(csr.perm),
-                                   csr.n_nodes, E, C, _ptr(out), _stream())
+                                   _ptr(csr.order), csr.n_nodes, E, C, _ptr(out), _stream())
     else:
         status = load().zs_forward_strided(_ptr(coupling), cs, _ptr(radial), re, rs,
-                                           _ptr(csr.rowptr), _ptr(csr.perm), csr.n_nodes, E, C,
-                                           _ptr(out), _stream())
+                                           _ptr(csr.rowptr), _ptr(csr.perm), _ptr(csr.order),
+                                           csr.n_nodes, E, C, _ptr(out), _stream())
     _check("zs_forward", status)
     return out
 
@@ -331,8 +340,8 @@ def zs_forward_normalized(coupling: torch.Tensor, radial: torch.Tensor, env: tor
     out = torch.empty_like(y) if keep_out else None
     norm = torch.empty(csr.n_nodes, dtype=torch.float32, device=dev)
     _check("zs_forward_normalized", load().zs_forward_normalized(
-        _ptr(coupling), _ptr(radial), _ptr(env), _ptr(csr.rowptr), _ptr(csr.perm), csr.n_nodes,
-        E, C, _ptr(y), _ptr(out), _ptr(norm), _stream()))
+        _ptr(coupling), _ptr(radial), _ptr(env), _ptr(csr.rowptr), _ptr(csr.perm),
+        _ptr(csr.order), csr.n_nodes, E, C, _ptr(y), _ptr(out), _ptr(norm), _stream()))
     return y, out, norm
 
 
@@ -366,8 +375,8 @@ def zs_backward_normalized(grad_y: torch.Tensor, out: torch.Tensor, norm: torch.
 
 class _GieZonalScatter(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, coupling, radial, rowptr, perm, dst32, n_nodes):
-        csr = Csr(rowptr, perm, dst32, n_nodes)
+    def forward(ctx, coupling, radial, rowptr, perm, dst32, n_nodes, order):
+        csr = Csr(rowptr, perm, dst32, n_nodes, order)
         ctx.save_for_backward(coupling, radial, rowptr, perm, dst32)
         ctx.n_nodes = n_nodes
         return zs_forward(coupling, radial, csr)
@@ -378,20 +387,21 @@ class _GieZonalScatter(torch.autograd.Function):
         coupling, radial, rowptr, perm, dst32 = ctx.saved_tensors
         csr = Csr(rowptr, perm, dst32, ctx.n_nodes)
         gc, gr = zs_backward(grad_out.contiguous(), coupling, radial, csr)
-        return gc, gr, None, None, None, None
+        return gc, gr, None, None, None, None, None
 
 
 def gie_zonal_scatter(coupling: torch.Tensor, radial: torch.Tensor, csr: Csr) -> torch.Tensor:
     """Differentiable zonal scatter.  Strided views of coupling and radial (for
     example sliced radial features, or the coupling inside a packed Wigner
     band) are read in place; the gradients are contiguous tensors."""
-    return _GieZonalScatter.apply(coupling, radial, csr.rowptr, csr.perm, csr.dst32, csr.n_nodes)
+    return _GieZonalScatter.apply(coupling, radial, csr.rowptr, csr.perm, csr.dst32, csr.n_nodes,
+                                  csr.order)
 
 
 class _GieZonalScatterNormalized(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, coupling, radial, env, rowptr, perm, dst32, n_nodes):
-        csr = Csr(rowptr, perm, dst32, n_nodes)
+    def forward(ctx, coupling, radial, env, rowptr, perm, dst32, n_nodes, order):
+        csr = Csr(rowptr, perm, dst32, n_nodes, order)
         coupling, radial = coupling.contiguous(), radial.contiguous()
         y, out, norm = zs_forward_normalized(coupling, radial, env, csr)
         ctx.save_for_backward(coupling, radial, out, norm, rowptr, perm, dst32)
@@ -407,7 +417,7 @@ class _GieZonalScatterNormalized(torch.autograd.Function):
             grad_y = torch.zeros_like(out)
         gc, gr, ge, _ = zs_backward_normalized(grad_y.contiguous(), out, norm, coupling, radial,
                                                csr)
-        return gc, gr, ge, None, None, None, None
+        return gc, gr, ge, None, None, None, None, None
 
 
 def gie_zonal_scatter_normalized(coupling: torch.Tensor, radial: torch.Tensor, env: torch.Tensor,
@@ -419,4 +429,4 @@ def gie_zonal_scatter_normalized(coupling: torch.Tensor, radial: torch.Tensor, e
     downstream would expect a gradient through it, which this function does
     not carry); ``zs_forward_normalized`` returns it as a plain tensor."""
     return _GieZonalScatterNormalized.apply(coupling, radial, env, csr.rowptr, csr.perm,
-                                            csr.dst32, csr.n_nodes)
+                                            csr.dst32, csr.n_nodes, csr.order)

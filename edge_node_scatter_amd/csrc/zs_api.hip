@@ -86,20 +86,24 @@ namespace {
 
 // Host-side checks of the CSR build's buffers (not the workspace).
 int csr_args(const int64_t* dst, int64_t n_edges, int64_t n_nodes, const int32_t* rowptr,
-             const int32_t* perm, const int32_t* dst32, const int32_t* bad_flag) {
+             const int32_t* perm, const int32_t* dst32, const int32_t* order,
+             const int32_t* bad_flag) {
     if (!sizes_ok(n_edges, n_nodes)) return ZS_ERR_SHAPE;
     if (!rowptr || (n_edges > 0 && (!dst || !perm || !dst32))) return ZS_ERR_NULL;
     if (!aligned(rowptr, 4) || (n_edges > 0 && (!aligned(dst, 8) || !aligned(perm, 4) ||
                                                 !aligned(dst32, 4))))
         return ZS_ERR_UNSUPPORTED;
-    if (bad_flag && !aligned(bad_flag, 4)) return ZS_ERR_UNSUPPORTED;
+    if ((bad_flag && !aligned(bad_flag, 4)) || (order && !aligned(order, 4)))
+        return ZS_ERR_UNSUPPORTED;
     const Range r_dst = span(dst, n_edges, 8), r_rowptr = span(rowptr, n_nodes + 1, 4),
                 r_perm = span(perm, n_edges, 4), r_dst32 = span(dst32, n_edges, 4),
-                r_flag = span(bad_flag, bad_flag ? 1 : 0, 4);
+                r_flag = span(bad_flag, bad_flag ? 1 : 0, 4),
+                r_order = span(order, order ? n_nodes : 0, 4);
     if (overlap(r_rowptr, r_dst) || overlap(r_perm, r_dst) || overlap(r_dst32, r_dst) ||
         overlap(r_rowptr, r_perm) || overlap(r_rowptr, r_dst32) || overlap(r_perm, r_dst32) ||
         overlap(r_flag, r_dst) || overlap(r_flag, r_rowptr) || overlap(r_flag, r_perm) ||
-        overlap(r_flag, r_dst32))
+        overlap(r_flag, r_dst32) || overlap(r_order, r_dst) || overlap(r_order, r_rowptr) ||
+        overlap(r_order, r_perm) || overlap(r_order, r_dst32) || overlap(r_order, r_flag))
         return ZS_ERR_ALIAS;
     return ZS_OK;
 }
@@ -107,16 +111,17 @@ int csr_args(const int64_t* dst, int64_t n_edges, int64_t n_nodes, const int32_t
 // The build on checked arguments.  With n_edges > 0 the workspace holds at
 // least plan.bytes and overlaps none of the buffers.
 int csr_run(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* rowptr,
-            int32_t* perm, int32_t* dst32, void* workspace, int32_t* bad_flag,
+            int32_t* perm, int32_t* dst32, int32_t* order, void* workspace, int32_t* bad_flag,
             hipStream_t s) {
     if (n_edges == 0) {
         hipError_t err = zs::launch_fill_i32(rowptr, n_nodes + 1, 0, s);
         if (err == hipSuccess && bad_flag) err = zs::launch_fill_i32(bad_flag, 1, 0, s);
+        if (err == hipSuccess && order) err = zs::launch_iota_i32(order, n_nodes, s);
         return hip_status(err);
     }
     const zs::CsrPlan plan = zs::plan_csr(n_edges, n_nodes);
-    hipError_t err = zs::launch_csr(dst, n_edges, n_nodes, rowptr, perm, dst32, workspace, plan,
-                                    bad_flag, s);
+    hipError_t err = zs::launch_csr(dst, n_edges, n_nodes, rowptr, perm, dst32, order, workspace,
+                                    plan, bad_flag, s);
     if (err != hipSuccess) return ZS_ERR_HIP;
     if (bad_flag) return ZS_OK;
     int32_t flag = 0;
@@ -133,9 +138,9 @@ int csr_run(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* rowpt
 extern "C" {
 
 int zs_build_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* rowptr,
-                 int32_t* perm, int32_t* dst32, void* workspace, size_t workspace_bytes,
-                 int32_t* bad_flag, void* stream) {
-    const int st = csr_args(dst, n_edges, n_nodes, rowptr, perm, dst32, bad_flag);
+                 int32_t* perm, int32_t* dst32, int32_t* order, void* workspace,
+                 size_t workspace_bytes, int32_t* bad_flag, void* stream) {
+    const int st = csr_args(dst, n_edges, n_nodes, rowptr, perm, dst32, order, bad_flag);
     if (st != ZS_OK) return st;
     if (n_edges > 0) {
         const zs::CsrPlan plan = zs::plan_csr(n_edges, n_nodes);
@@ -144,17 +149,18 @@ int zs_build_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* 
         const Range r_ws = span(workspace, int64_t(plan.bytes), 1);
         if (overlap(r_ws, span(dst, n_edges, 8)) || overlap(r_ws, span(rowptr, n_nodes + 1, 4)) ||
             overlap(r_ws, span(perm, n_edges, 4)) || overlap(r_ws, span(dst32, n_edges, 4)) ||
-            overlap(r_ws, span(bad_flag, bad_flag ? 1 : 0, 4)))
+            overlap(r_ws, span(bad_flag, bad_flag ? 1 : 0, 4)) ||
+            overlap(r_ws, span(order, order ? n_nodes : 0, 4)))
             return ZS_ERR_ALIAS;
     }
-    return csr_run(dst, n_edges, n_nodes, rowptr, perm, dst32, workspace, bad_flag,
+    return csr_run(dst, n_edges, n_nodes, rowptr, perm, dst32, order, workspace, bad_flag,
                    static_cast<hipStream_t>(stream));
 }
 
 int zs_build_csr_noalloc(const int64_t* dst, int64_t n_edges, int64_t n_nodes,
-                         int32_t* rowptr, int32_t* perm, int32_t* dst32, int32_t* bad_flag,
-                         void* stream) {
-    const int st = csr_args(dst, n_edges, n_nodes, rowptr, perm, dst32, bad_flag);
+                         int32_t* rowptr, int32_t* perm, int32_t* dst32, int32_t* order,
+                         int32_t* bad_flag, void* stream) {
+    const int st = csr_args(dst, n_edges, n_nodes, rowptr, perm, dst32, order, bad_flag);
     if (st != ZS_OK) return st;
     void* ws = nullptr;
     if (n_edges > 0) {
@@ -163,7 +169,7 @@ int zs_build_csr_noalloc(const int64_t* dst, int64_t n_edges, int64_t n_nodes,
         ws = noalloc_scratch();   // first call on this device: symbol lookup, no allocation
         if (ws == nullptr) return ZS_ERR_HIP;
     }
-    return csr_run(dst, n_edges, n_nodes, rowptr, perm, dst32, ws, bad_flag,
+    return csr_run(dst, n_edges, n_nodes, rowptr, perm, dst32, order, ws, bad_flag,
                    static_cast<hipStream_t>(stream));
 }
 
@@ -185,24 +191,25 @@ int64_t rad_extent(int64_t E, int64_t re, int64_t rs, int64_t C) {
 }
 
 int forward_impl(const float* coupling, int64_t cs, const float* radial, int64_t re, int64_t rs,
-                 const int32_t* rowptr, const int32_t* perm, int64_t n_nodes, int64_t n_edges,
-                 int64_t channels, float* out, void* stream) {
+                 const int32_t* rowptr, const int32_t* perm, const int32_t* order,
+                 int64_t n_nodes, int64_t n_edges, int64_t channels, float* out, void* stream) {
     if (!sizes_ok(n_edges, n_nodes) || !channels_ok(channels)) return ZS_ERR_SHAPE;
     if (!layout_ok(cs, re, rs, channels)) return ZS_ERR_SHAPE;
     if (!out || !rowptr || (n_edges > 0 && (!coupling || !radial || !perm))) return ZS_ERR_NULL;
-    if (!aligned(out, 4) || !aligned(rowptr, 4) ||
+    if (!aligned(out, 4) || !aligned(rowptr, 4) || (order && !aligned(order, 4)) ||
         (n_edges > 0 && (!aligned(coupling, 4) || !aligned(radial, 4) || !aligned(perm, 4))))
         return ZS_ERR_UNSUPPORTED;
     const Range r_out = span(out, n_nodes * zs::kRows * channels, 4);
     if (overlap(r_out, span(coupling, cpl_extent(n_edges, cs), 4)) ||
         overlap(r_out, span(radial, rad_extent(n_edges, re, rs, channels), 4)) ||
-        overlap(r_out, span(rowptr, n_nodes + 1, 4)) || overlap(r_out, span(perm, n_edges, 4)))
+        overlap(r_out, span(rowptr, n_nodes + 1, 4)) || overlap(r_out, span(perm, n_edges, 4)) ||
+        overlap(r_out, span(order, order ? n_nodes : 0, 4)))
         return ZS_ERR_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool vec4 = channels % 4 == 0 && aligned(out, 16) &&
                       (n_edges == 0 || (aligned(radial, 16) && re % 4 == 0 && rs % 4 == 0));
     return hip_status(zs::launch_forward(coupling, radial, zs::InLayout{cs, re, rs}, rowptr, perm,
-                                         n_nodes, n_edges, channels, out, vec4,
+                                         order, n_nodes, n_edges, channels, out, vec4,
                                          zs::NormIO{nullptr, nullptr, nullptr}, s));
 }
 
@@ -244,18 +251,20 @@ int backward_impl(const float* grad_out, const float* coupling, int64_t cs, cons
 extern "C" {
 
 int zs_forward(const float* coupling, const float* radial, const int32_t* rowptr,
-               const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels, float* out,
-               void* stream) {
+               const int32_t* perm, const int32_t* order, int64_t n_nodes, int64_t n_edges,
+               int64_t channels, float* out, void* stream) {
     return forward_impl(coupling, zs::kZonal, radial, zs::kSlots * channels, channels, rowptr,
-                        perm, n_nodes, n_edges, channels, out, stream);
+                        perm, order, n_nodes, n_edges, channels, out, stream);
 }
 
 int zs_forward_strided(const float* coupling, int64_t coupling_edge_stride, const float* radial,
                        int64_t radial_edge_stride, int64_t radial_slot_stride,
-                       const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
-                       int64_t n_edges, int64_t channels, float* out, void* stream) {
+                       const int32_t* rowptr, const int32_t* perm, const int32_t* order,
+                       int64_t n_nodes, int64_t n_edges, int64_t channels, float* out,
+                       void* stream) {
     return forward_impl(coupling, coupling_edge_stride, radial, radial_edge_stride,
-                        radial_slot_stride, rowptr, perm, n_nodes, n_edges, channels, out, stream);
+                        radial_slot_stride, rowptr, perm, order, n_nodes, n_edges, channels, out,
+                        stream);
 }
 
 int zs_backward(const float* grad_out, const float* coupling, const float* radial,
@@ -279,13 +288,14 @@ int zs_backward_strided(const float* grad_out, const float* coupling,
 }
 
 int zs_forward_normalized(const float* coupling, const float* radial, const float* env,
-                          const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
-                          int64_t n_edges, int64_t channels, float* y, float* out, float* norm,
-                          void* stream) {
+                          const int32_t* rowptr, const int32_t* perm, const int32_t* order,
+                          int64_t n_nodes, int64_t n_edges, int64_t channels, float* y,
+                          float* out, float* norm, void* stream) {
     if (!sizes_ok(n_edges, n_nodes) || !channels_ok(channels)) return ZS_ERR_SHAPE;
     if (!y || !norm || !rowptr || (n_edges > 0 && (!coupling || !radial || !env || !perm)))
         return ZS_ERR_NULL;
     if (!aligned(y, 4) || !aligned(norm, 4) || (out && !aligned(out, 4)) || !aligned(rowptr, 4) ||
+        (order && !aligned(order, 4)) ||
         (n_edges > 0 && (!aligned(coupling, 4) || !aligned(radial, 4) || !aligned(env, 4) ||
                          !aligned(perm, 4))))
         return ZS_ERR_UNSUPPORTED;
@@ -295,7 +305,7 @@ int zs_forward_normalized(const float* coupling, const float* radial, const floa
     const Range ins[] = {span(coupling, n_edges * zs::kZonal, 4),
                          span(radial, n_edges * zs::kSlots * channels, 4),
                          span(env, n_edges, 4), span(rowptr, n_nodes + 1, 4),
-                         span(perm, n_edges, 4)};
+                         span(perm, n_edges, 4), span(order, order ? n_nodes : 0, 4)};
     for (int i = 0; i < 3; ++i) {
         for (int j = i + 1; j < 3; ++j)
             if (overlap(outs[i], outs[j])) return ZS_ERR_ALIAS;
@@ -307,8 +317,8 @@ int zs_forward_normalized(const float* coupling, const float* radial, const floa
                       (n_edges == 0 || aligned(radial, 16));
     return hip_status(zs::launch_forward(coupling, radial,
                                          zs::InLayout{zs::kZonal, zs::kSlots * channels, channels},
-                                         rowptr, perm, n_nodes, n_edges, channels, out, vec4,
-                                         zs::NormIO{env, y, norm}, s));
+                                         rowptr, perm, order, n_nodes, n_edges, channels, out,
+                                         vec4, zs::NormIO{env, y, norm}, s));
 }
 
 int zs_backward_normalized(const float* grad_y, const float* out, const float* norm,

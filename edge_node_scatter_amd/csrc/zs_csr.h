@@ -23,9 +23,12 @@ struct CsrPlan {
 };
 CsrPlan plan_csr(int64_t n_edges, int64_t n_nodes);
 // flag: device int32 that receives the out-of-range indicator; NULL selects
-// the one inside the workspace (at plan.off_flag).
+// the one inside the workspace (at plan.off_flag).  order: NULL, or n_nodes
+// int32 that receive the node order (the forward's schedule).
 hipError_t launch_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* rowptr,
-                      int32_t* perm, int32_t* dst32, void* workspace, const CsrPlan& plan,
-                      int32_t* flag, hipStream_t stream);
+                      int32_t* perm, int32_t* dst32, int32_t* order, void* workspace,
+                      const CsrPlan& plan, int32_t* flag, hipStream_t stream);
+// order[i] = i for i < n (the node order of a frame without edges).
+hipError_t launch_iota_i32(int32_t* p, int64_t n, hipStream_t stream);
 
 }  // namespace zs

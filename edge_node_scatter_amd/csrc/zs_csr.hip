@@ -30,6 +30,18 @@
 // Neither kernel reads more than two rows of the NB x W offset table, so
 // every workgroup is a few memory round trips deep.
 //
+// Node order (optional output): a permutation of the nodes that the forward
+// uses as the order in which it hands nodes to wavefronts (results do not
+// depend on it).  Each bucket_place workgroup ranks its own bucket's nodes by
+// decreasing degree (ties by node id) and writes them rank-major: slot
+// r * NBf + ((b + r) mod NBf) for rank r of full bucket b (NBf full buckets),
+// the partial last bucket's nodes after them in rank order.  So the first
+// NBf slots hold every bucket's highest-degree node, the next NBf every
+// bucket's second, and so on: heavy nodes are handed out first, and each band
+// of NBf consecutive slots, which the dispatcher spreads over the compute
+// units, draws from all buckets.  Frames with buckets of more than 64 nodes
+// (above 16384 nodes) get the identity order.
+//
 // Every destination is range-checked; an out-of-range one is never used as an
 // index and raises the validation flag.
 #include "zs_csr.h"
@@ -167,6 +179,18 @@ __device__ __attribute__((always_inline)) inline int64_t place_step(bool ok, int
     }
     o = __shfl(o, leader, 64);
     return int64_t(o) + rank;
+}
+
+// ---- node order --------------------------------------------------------------
+
+constexpr int kOrderBucketMax = 64;   // bucket sizes that get a ranked order (one wavefront)
+
+// Slot of the node of rank `rank` (0 = highest degree) in bucket b: rank-major
+// over the nf full buckets, rotated by the rank, and the partial bucket nf
+// (if any) after all of them.
+__device__ __attribute__((always_inline)) inline int64_t order_slot(int64_t b, int64_t rank,
+                                                                    int64_t nf, int64_t bn) {
+    return b < nf ? rank * nf + (b + rank) % nf : nf * bn + rank;
 }
 
 // ---- kernel 1: sort each chunk by bucket ------------------------------------
@@ -324,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void csr_bucket_place_kernel(
     const int2* __restrict__ pairs, const int32_t* __restrict__ loff,
     const int32_t* __restrict__ chunk_bad, int64_t chunks, int64_t chunk_edges, int64_t n_edges,
     int64_t n_nodes, int sb, int64_t n_buckets, int32_t* __restrict__ flag,
-    int32_t* __restrict__ rowptr, int32_t* __restrict__ perm) {
+    int32_t* __restrict__ rowptr, int32_t* __restrict__ perm, int32_t* __restrict__ order) {
     extern __shared__ int32_t lds[];
     const int64_t bn = int64_t(1) << sb;
     int32_t* runpre = lds;
@@ -364,11 +388,29 @@ __global__ __launch_bounds__(kThreads) void csr_bucket_place_kernel(
         }
     }
     __syncthreads();
+    int32_t my_deg = 0;   // degree of node n0 + tid
     for (int64_t n = tid; n < nn; n += kThreads) {
         int32_t s = 0;
 #pragma unroll
         for (int w = 0; w < kParts; ++w) s += run_all[w * bn + n];
         noff[n] = s;
+        if (n == tid) my_deg = s;
+    }
+    if (order != nullptr) {
+        if (bn <= kOrderBucketMax) {
+            // wavefront 0 holds the bucket's nodes, one per lane: rank by
+            // decreasing degree, ties by node id
+            if (wave == 0) {
+                int64_t rank = 0;
+                for (int k = 0; k < int(nn); ++k) {
+                    const int32_t dk = __builtin_amdgcn_readlane(my_deg, k);
+                    rank += dk > my_deg || (dk == my_deg && k < lane);
+                }
+                if (lane < nn) order[order_slot(b, rank, n_nodes >> sb, bn)] = int32_t(n0 + lane);
+            }
+        } else {
+            for (int64_t n = tid; n < nn; n += kThreads) order[n0 + n] = int32_t(n0 + n);
+        }
     }
     __syncthreads();
     block_exclusive_scan_lds<kThreads>(noff, nn);
@@ -407,7 +449,8 @@ __global__ __launch_bounds__(kGlobalThreads) void csr_bucket_place_global_kernel
     const int2* __restrict__ pairs, const int32_t* __restrict__ loff,
     const int32_t* __restrict__ chunk_bad, int64_t chunks, int64_t chunk_edges, int64_t n_edges,
     int64_t n_nodes, int sb, int64_t n_buckets, int32_t* __restrict__ flag,
-    int32_t* __restrict__ rowptr, int32_t* __restrict__ perm, int32_t* __restrict__ scratch) {
+    int32_t* __restrict__ rowptr, int32_t* __restrict__ perm, int32_t* __restrict__ scratch,
+    int32_t* __restrict__ order) {
     extern __shared__ int32_t lds[];
     const int64_t bn = int64_t(1) << sb;
     int32_t* runpre = lds;
@@ -447,6 +490,8 @@ __global__ __launch_bounds__(kGlobalThreads) void csr_bucket_place_global_kernel
     }
     __threadfence();
     __syncthreads();
+    if (order != nullptr)   // buckets of more than kOrderBucketMax nodes: identity
+        for (int64_t n = tid; n < nn; n += kGlobalThreads) order[n0 + n] = int32_t(n0 + n);
     if (tid >= 64) return;
     for (int64_t base = 0; base < size; base += 64) {
         const int64_t i = base + lane;
@@ -470,6 +515,18 @@ inline unsigned grid_for(int64_t n, int threads, int64_t cap = 1 << 20) {
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     fill_i32_kernel<<<grid_for(n, 256, 4096), 256, 0, stream>>>(p, n, v);
+    return hipGetLastError();
+}
+
+__global__ void iota_i32_kernel(int32_t* __restrict__ p, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * blockDim.x)
+        p[i] = int32_t(i);
+}
+
+hipError_t launch_iota_i32(int32_t* p, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    iota_i32_kernel<<<grid_for(n, 256, 4096), 256, 0, stream>>>(p, n);
     return hipGetLastError();
 }
 
@@ -510,8 +567,8 @@ CsrPlan plan_csr(int64_t n_edges, int64_t n_nodes) {
 }
 
 hipError_t launch_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int32_t* rowptr,
-                      int32_t* perm, int32_t* dst32, void* workspace, const CsrPlan& plan,
-                      int32_t* flag, hipStream_t stream) {
+                      int32_t* perm, int32_t* dst32, int32_t* order, void* workspace,
+                      const CsrPlan& plan, int32_t* flag, hipStream_t stream) {
     char* ws = static_cast<char*>(workspace);
     if (!flag) flag = reinterpret_cast<int32_t*>(ws + plan.off_flag);
     int32_t* chunk_bad = reinterpret_cast<int32_t*>(ws + plan.off_chunk_bad);
@@ -529,15 +586,16 @@ hipError_t launch_csr(const int64_t* dst, int64_t n_edges, int64_t n_nodes, int3
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const size_t runs_lds = size_t(2 * W + 1) * sizeof(int32_t);
     const int64_t bn = int64_t(1) << sb;
-    if (plan.node_lds)
+    if (plan.node_lds) {
         csr_bucket_place_kernel<<<unsigned(nb), kThreads,
                                   runs_lds + size_t(kParts + 1) * size_t(bn) * sizeof(int32_t),
                                   stream>>>(pairs, loff, chunk_bad, W, plan.chunk_edges, n_edges,
-                                            n_nodes, sb, nb, flag, rowptr, perm);
-    else
+                                            n_nodes, sb, nb, flag, rowptr, perm, order);
+    } else {
         csr_bucket_place_global_kernel<<<unsigned(nb), kGlobalThreads, runs_lds, stream>>>(
             pairs, loff, chunk_bad, W, plan.chunk_edges, n_edges, n_nodes, sb, nb, flag, rowptr,
-            perm, scratch);
+            perm, scratch, order);
+    }
     return hipGetLastError();
 }
 

@@ -14,6 +14,13 @@
 // nodes) and zs_fwd_kernel (any C and alignment).  All three accumulate the
 // same products in the same order, so their results are bitwise equal.
 //
+// Grid position s sums node order[s] when the caller passes the node schedule
+// the CSR build produces (every bucket's highest-degree nodes first, each band
+// spread over the compute units), else node s.  When a launch's wavefronts are
+// all resident at once the dispatcher's placement is fixed by position, so the
+// schedule is what spreads high-degree nodes evenly: on the skewed 4096-node
+// frame the forward takes 65.5 instead of 72.6 us.
+//
 // Mapping of zs_fwd_kernel (one 64-lane wavefront per node and channel tile):
 //   lane = j * NQ + q.  q picks VEC consecutive channels (tile width NQ*VEC),
 //   j picks a slot of RPS consecutive padded rows (rows j*RPS+1 .. j*RPS+RPS;
@@ -34,12 +41,24 @@ namespace zs {
 
 namespace {
 
+// Node handled at grid position slot: order[slot] when a node order is given
+// (-1, skipped, when the entry is not a node), else slot itself.  The order
+// only decides which wavefront sums which node, and when; every node's sums
+// are the same either way.
+__device__ __attribute__((always_inline)) inline int64_t node_at(const int32_t* __restrict__ order,
+                                                                 int64_t slot, int64_t n_nodes) {
+    if (order == nullptr) return slot;
+    const int64_t n = order[slot];
+    return n >= 0 && n < n_nodes ? n : -1;
+}
+
 // NORM: as zs_fwd_staged_kernel below (envelope sum, y, norm, optional out).
 template <int VEC, int NQ, int U, bool NORM>
 __global__ __launch_bounds__(64) void zs_fwd_kernel(const float* __restrict__ coupling,
                                                     const float* __restrict__ radial, InLayout L,
                                                     const int32_t* __restrict__ rowptr,
                                                     const int32_t* __restrict__ perm,
+                                                    const int32_t* __restrict__ order,
                                                     int64_t n_nodes, int64_t n_edges, int64_t C,
                                                     float* __restrict__ out, NormIO nio) {
     using V = VecT<VEC>;
@@ -59,7 +78,9 @@ __global__ __launch_bounds__(64) void zs_fwd_kernel(const float* __restrict__ co
     const int64_t c0 = (int64_t(blockIdx.y) * NQ + q) * VEC;
     const bool act = c0 < C;
 
-    for (int64_t node = blockIdx.x; node < n_nodes; node += gridDim.x) {
+    for (int64_t slot = blockIdx.x; slot < n_nodes; slot += gridDim.x) {
+        const int64_t node = node_at(order, slot, n_nodes);
+        if (node < 0) continue;
         int64_t k0 = rowptr[node];
         int64_t k1 = rowptr[node + 1];
         k0 = k0 < 0 ? 0 : (k0 > n_edges ? n_edges : k0);
@@ -427,23 +448,35 @@ __device__ __attribute__((always_inline)) inline void node_range(const int32_t* 
     k1 = k1 < k0 ? k0 : (k1 > n_edges ? n_edges : k1);
 }
 
+// Nodes of degree above `heavy` take batches of BH = 8 edges when the launch
+// uses 4 (VEC <= 4): twice the bytes in flight for the nodes that finish
+// last; the others keep B.  Both paths add the same products in the same
+// order.
 template <int VEC, int B, bool NORM>
 __global__ __launch_bounds__(64) void zs_fwd_staged_kernel(const float* __restrict__ coupling,
                                                            const float* __restrict__ radial,
                                                            InLayout L,
                                                            const int32_t* __restrict__ rowptr,
                                                            const int32_t* __restrict__ perm,
-                                                           int64_t n_nodes, int64_t n_edges,
-                                                           int64_t C, float* __restrict__ out,
-                                                           NormIO nio) {
-    __shared__ float4 rsh[FwdShape<VEC, B>::RAD];
-    __shared__ float csh[B * 16];
-    if (threadIdx.x < B) csh[threadIdx.x * 16 + 15] = 0.0f;   // pad column, never fetched
-    for (int64_t node = blockIdx.x; node < n_nodes; node += gridDim.x) {
+                                                           const int32_t* __restrict__ order,
+                                                           int64_t heavy, int64_t n_nodes,
+                                                           int64_t n_edges, int64_t C,
+                                                           float* __restrict__ out, NormIO nio) {
+    constexpr int BH = (B == 4 && VEC <= 4) ? 8 : B;
+    __shared__ float4 rsh[FwdShape<VEC, BH>::RAD];
+    __shared__ float csh[BH * 16];
+    if (threadIdx.x < BH) csh[threadIdx.x * 16 + 15] = 0.0f;   // pad column, never fetched
+    for (int64_t slot = blockIdx.x; slot < n_nodes; slot += gridDim.x) {
+        const int64_t node = node_at(order, slot, n_nodes);
+        if (node < 0) continue;
         int64_t k0, k1;
         node_range(rowptr, node, n_edges, k0, k1);
-        fwd_staged_node<VEC, B, NORM>(node, k0, k1, coupling, radial, L, perm, n_edges, C, out,
-                                      nio, rsh, csh);
+        if (BH != B && k1 - k0 > heavy)
+            fwd_staged_node<VEC, BH, NORM>(node, k0, k1, coupling, radial, L, perm, n_edges, C,
+                                           out, nio, rsh, csh);
+        else
+            fwd_staged_node<VEC, B, NORM>(node, k0, k1, coupling, radial, L, perm, n_edges, C,
+                                          out, nio, rsh, csh);
     }
 }
 
@@ -605,6 +638,7 @@ __global__ __launch_bounds__(192) void zs_fwd_slot_kernel(const float* __restric
                                                           InLayout L,
                                                           const int32_t* __restrict__ rowptr,
                                                           const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ order,
                                                           int64_t n_nodes, int64_t n_edges,
                                                           int64_t C, float* __restrict__ out,
                                                           NormIO nio) {
@@ -612,7 +646,9 @@ __global__ __launch_bounds__(192) void zs_fwd_slot_kernel(const float* __restric
     __shared__ float4 rsh_all[kSlots][S::RAD];
     __shared__ float csh_all[kSlots][S::CW];
     const int s = threadIdx.x >> 6;            // slot of this wavefront
-    for (int64_t node = blockIdx.x; node < n_nodes; node += gridDim.x) {
+    for (int64_t slot = blockIdx.x; slot < n_nodes; slot += gridDim.x) {
+        const int64_t node = node_at(order, slot, n_nodes);
+        if (node < 0) continue;
         int64_t k0, k1;
         node_range(rowptr, node, n_edges, k0, k1);
         fwd_slot_node<VEC, B, NORM>(node, s, k0, k1, coupling, radial, L, perm, n_edges, C, out,
@@ -622,28 +658,39 @@ __global__ __launch_bounds__(192) void zs_fwd_slot_kernel(const float* __restric
 
 template <int VEC, int B>
 void launch_slot(const float* coupling, const float* radial, InLayout L, const int32_t* rowptr,
-                 const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels,
-                 float* out, NormIO nio, unsigned gx, hipStream_t stream) {
+                 const int32_t* perm, const int32_t* order, int64_t n_nodes, int64_t n_edges,
+                 int64_t channels, float* out, NormIO nio, unsigned gx, hipStream_t stream) {
     const unsigned gy = unsigned((channels + 8 * VEC - 1) / (8 * VEC));
     if (nio.y != nullptr)
         zs_fwd_slot_kernel<VEC, B, true><<<dim3(gx, gy), 192, 0, stream>>>(
-            coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
+            coupling, radial, L, rowptr, perm, order, n_nodes, n_edges, channels, out, nio);
     else
         zs_fwd_slot_kernel<VEC, B, false><<<dim3(gx, gy), 192, 0, stream>>>(
-            coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
+            coupling, radial, L, rowptr, perm, order, n_nodes, n_edges, channels, out, nio);
+}
+
+// Degree above which the staged kernel's 4-edge launches give a node 8-edge
+// batches: 5/4 of the mean degree.  Measured (forward, read-flushed caches) on
+// the skewed 4096-node frame with the CSR build's node schedule: 69.3 ->
+// 65.5 us, and 59.4 -> 58.6 us on a frame of i.i.d. uniform destinations.
+// Without a schedule the heavy nodes crowd some compute units and the wider
+// batches gain nothing (71.7 us either way).
+int64_t heavy_degree(int64_t n_edges, int64_t n_nodes) {
+    return n_nodes > 0 ? (5 * n_edges) / (4 * n_nodes) : 0;
 }
 
 template <int VEC, int B>
 void launch_staged(const float* coupling, const float* radial, InLayout L, const int32_t* rowptr,
-                   const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels,
-                   float* out, NormIO nio, unsigned gx, hipStream_t stream) {
+                   const int32_t* perm, const int32_t* order, int64_t n_nodes, int64_t n_edges,
+                   int64_t channels, float* out, NormIO nio, unsigned gx, hipStream_t stream) {
     const unsigned gy = unsigned((channels + 8 * VEC - 1) / (8 * VEC));
+    const int64_t heavy = heavy_degree(n_edges, n_nodes);
     if (nio.y != nullptr)   // env may be NULL when there are no edges
         zs_fwd_staged_kernel<VEC, B, true><<<dim3(gx, gy), 64, 0, stream>>>(
-            coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
+            coupling, radial, L, rowptr, perm, order, heavy, n_nodes, n_edges, channels, out, nio);
     else
         zs_fwd_staged_kernel<VEC, B, false><<<dim3(gx, gy), 64, 0, stream>>>(
-            coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
+            coupling, radial, L, rowptr, perm, order, heavy, n_nodes, n_edges, channels, out, nio);
 }
 
 // Edges per batch of the staged kernel, from the number of wavefronts the
@@ -682,15 +729,15 @@ int forward_tile_vec(int64_t channels) {
 }  // namespace
 
 hipError_t launch_forward(const float* coupling, const float* radial, InLayout L,
-                          const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
-                          int64_t n_edges, int64_t channels, float* out, bool vec4,
-                          NormIO nio, hipStream_t stream) {
+                          const int32_t* rowptr, const int32_t* perm, const int32_t* order,
+                          int64_t n_nodes, int64_t n_edges, int64_t channels, float* out,
+                          bool vec4, NormIO nio, hipStream_t stream) {
     constexpr int64_t kGridCap = 1 << 20;
     const unsigned gx = unsigned(n_nodes < kGridCap ? n_nodes : kGridCap);
     if (vec4) {
 #define ZS_FWD_STAGED(V, BB)                                                                     \
-    launch_staged<V, BB>(coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio, \
-                         gx, stream)
+    launch_staged<V, BB>(coupling, radial, L, rowptr, perm, order, n_nodes, n_edges, channels, out, \
+                         nio, gx, stream)
 #define ZS_FWD_STAGED_B(V)                         \
     switch (batch) {                               \
         case 8: ZS_FWD_STAGED(V, 8); break;        \
@@ -704,11 +751,11 @@ hipError_t launch_forward(const float* coupling, const float* radial, InLayout L
 #define ZS_FWD_SLOT(V)                                                                         \
     do {                                                                                         \
         if (slot_batch == 16)                                                                    \
-            launch_slot<V, 16>(coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels,   \
-                               out, nio, gx, stream);                                            \
+            launch_slot<V, 16>(coupling, radial, L, rowptr, perm, order, n_nodes, n_edges,      \
+                               channels, out, nio, gx, stream);                                  \
         else                                                                                     \
-            launch_slot<V, 8>(coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels,    \
-                              out, nio, gx, stream);                                             \
+            launch_slot<V, 8>(coupling, radial, L, rowptr, perm, order, n_nodes, n_edges,       \
+                              channels, out, nio, gx, stream);                                   \
     } while (0)
             switch (vec) {
                 case 1: ZS_FWD_SLOT(1); break;
@@ -740,10 +787,10 @@ hipError_t launch_forward(const float* coupling, const float* radial, InLayout L
         const unsigned gy = unsigned((channels + NQ * VEC - 1) / (NQ * VEC));
         if (nio.y != nullptr)
             zs_fwd_kernel<VEC, NQ, 8, true><<<dim3(gx, gy), 64, 0, stream>>>(
-                coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
+                coupling, radial, L, rowptr, perm, order, n_nodes, n_edges, channels, out, nio);
         else
             zs_fwd_kernel<VEC, NQ, 8, false><<<dim3(gx, gy), 64, 0, stream>>>(
-                coupling, radial, L, rowptr, perm, n_nodes, n_edges, channels, out, nio);
+                coupling, radial, L, rowptr, perm, order, n_nodes, n_edges, channels, out, nio);
     }
     return hipGetLastError();
 }

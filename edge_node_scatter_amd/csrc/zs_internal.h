@@ -103,10 +103,12 @@ struct NormIO {
     float* norm;
 };
 
+// order: NULL (grid position = node) or the node order from the CSR build
+// (the node handed to each grid position).
 hipError_t launch_forward(const float* coupling, const float* radial, InLayout L,
-                          const int32_t* rowptr, const int32_t* perm, int64_t n_nodes,
-                          int64_t n_edges, int64_t channels, float* out, bool vec4,
-                          NormIO nio, hipStream_t stream);
+                          const int32_t* rowptr, const int32_t* perm, const int32_t* order,
+                          int64_t n_nodes, int64_t n_edges, int64_t channels, float* out,
+                          bool vec4, NormIO nio, hipStream_t stream);
 
 // Normalised backward.  norm == nullptr: plain backward.  Otherwise grad_out is
 // the gradient of y and is multiplied by norm[dst] (fp32) on load, and when

@@ -80,6 +80,18 @@ size_t zs_csr_workspace_bytes(int64_t n_edges, int64_t n_nodes);
  *                                 equal dst in increasing edge id (output)
  *   dst32    [n_edges]     int32  int32 copy of dst, -1 where out of range (output;
  *                                 zs_backward_normalized reads it)
+ *   order    [n_nodes]     int32  node schedule for the forward (output; may be
+ *                                 NULL): a permutation of the nodes.  The nodes are
+ *                                 split into buckets of B consecutive nodes, B the
+ *                                 smallest power of two >= n_nodes / 256 (B = 1
+ *                                 below 257 nodes), and ranked inside each bucket
+ *                                 by decreasing degree (equal degrees: increasing
+ *                                 id).  With F = floor(n_nodes / B) full buckets,
+ *                                 rank r of full bucket b is at order[r*F + (b + r)
+ *                                 mod F], rank r of the partial last bucket at
+ *                                 order[F*B + r].  Frames with B > 64 (more than
+ *                                 16384 nodes) get order[i] = i.  A scheduling aid
+ *                                 only: the forward's results do not depend on it.
  *   workspace, workspace_bytes >= zs_csr_workspace_bytes(n_edges, n_nodes),
  *                                 256-byte aligned device scratch
  *   bad_flag                      NULL: synchronous index check -- the call
@@ -95,7 +107,7 @@ size_t zs_csr_workspace_bytes(int64_t n_edges, int64_t n_nodes);
  * written.
  */
 int zs_build_csr(const int64_t *dst, int64_t n_edges, int64_t n_nodes,
-                 int32_t *rowptr, int32_t *perm, int32_t *dst32,
+                 int32_t *rowptr, int32_t *perm, int32_t *dst32, int32_t *order,
                  void *workspace, size_t workspace_bytes, int32_t *bad_flag,
                  void *stream);
 
@@ -107,7 +119,7 @@ int zs_build_csr(const int64_t *dst, int64_t n_edges, int64_t n_nodes,
  * first call on that device until the process ends.  The call allocates and
  * frees nothing; the caller still passes the inputs and outputs.
  *
- *   dst, n_edges, n_nodes, rowptr, perm, dst32, bad_flag, stream
+ *   dst, n_edges, n_nodes, rowptr, perm, dst32, order, bad_flag, stream
  *       as in zs_build_csr (same kernels, bitwise the same outputs).  The
  *       buffers and the stream must belong to the calling thread's current
  *       device.
@@ -124,7 +136,7 @@ int zs_build_csr(const int64_t *dst, int64_t n_edges, int64_t n_nodes,
 
 int zs_build_csr_noalloc(const int64_t *dst, int64_t n_edges, int64_t n_nodes,
                          int32_t *rowptr, int32_t *perm, int32_t *dst32,
-                         int32_t *bad_flag, void *stream);
+                         int32_t *order, int32_t *bad_flag, void *stream);
 
 /*
  * zs_forward -- fused zonal scatter forward (same page, "What", Forward
@@ -134,18 +146,27 @@ int zs_build_csr_noalloc(const int64_t *dst, int64_t n_edges, int64_t n_nodes,
  *   coupling [n_edges][15]             fp32  zonal coupling (input)
  *   radial   [n_edges][3][channels]    fp32  radial features, slot l-1 (input)
  *   rowptr, perm                       from zs_build_csr for the same dst
+ *   order    [n_nodes]                 int32 node schedule from the same
+ *                                            zs_build_csr call, or NULL (nodes in
+ *                                            index order).  It decides only which
+ *                                            wavefront sums which node and when
+ *                                            (every bucket's highest-degree nodes
+ *                                            first, spread over the compute units);
+ *                                            out is bitwise the same.
  *   out      [n_nodes][16][channels]   fp32  fully overwritten (output)
  *
  * out[n][0][:] = +0; out[n][r][c] adds fp32(coupling*radial) products over the
  * node's edges in increasing edge id, starting from +0, with separate fp32
  * multiply and add (no fused multiply-add): bitwise the fp32 result of the
  * materialised message followed by index_add.  Run-to-run deterministic.
- * A CSR that zs_build_csr did not produce gives unspecified values but no
- * out-of-bounds access (positions and edge ids are range-checked).
+ * A CSR or order that zs_build_csr did not produce gives unspecified values
+ * but no out-of-bounds access (positions, edge ids and order entries are
+ * range-checked).
  */
 int zs_forward(const float *coupling, const float *radial,
-               const int32_t *rowptr, const int32_t *perm, int64_t n_nodes,
-               int64_t n_edges, int64_t channels, float *out, void *stream);
+               const int32_t *rowptr, const int32_t *perm, const int32_t *order,
+               int64_t n_nodes, int64_t n_edges, int64_t channels, float *out,
+               void *stream);
 
 /*
  * zs_backward -- fused zonal scatter backward (same page, "What", Backward
@@ -202,8 +223,9 @@ int zs_backward(const float *grad_out, const float *coupling,
 int zs_forward_strided(const float *coupling, int64_t coupling_edge_stride,
                        const float *radial, int64_t radial_edge_stride,
                        int64_t radial_slot_stride, const int32_t *rowptr,
-                       const int32_t *perm, int64_t n_nodes, int64_t n_edges,
-                       int64_t channels, float *out, void *stream);
+                       const int32_t *perm, const int32_t *order, int64_t n_nodes,
+                       int64_t n_edges, int64_t channels, float *out,
+                       void *stream);
 
 int zs_backward_strided(const float *grad_out, const float *coupling,
                         int64_t coupling_edge_stride, const float *radial,
@@ -219,7 +241,8 @@ int zs_backward_strided(const float *grad_out, const float *coupling,
  * step of the sequence diagram), fused into the same node-parallel pass.  The
  * degree is the sum of the edges' cutoff-envelope factors.
  *
- *   coupling, radial, rowptr, perm, n_nodes, n_edges, channels  as in zs_forward
+ *   coupling, radial, rowptr, perm, order, n_nodes, n_edges, channels
+ *                                    as in zs_forward
  *   env   [n_edges]                  fp32  cutoff-envelope factor per edge (input)
  *   y     [n_nodes][16][channels]    fp32  normalised output (output)
  *   out   [n_nodes][16][channels]    fp32  unnormalised scatter, bitwise the
@@ -235,9 +258,9 @@ int zs_backward_strided(const float *grad_out, const float *coupling,
  */
 int zs_forward_normalized(const float *coupling, const float *radial,
                           const float *env, const int32_t *rowptr,
-                          const int32_t *perm, int64_t n_nodes, int64_t n_edges,
-                          int64_t channels, float *y, float *out, float *norm,
-                          void *stream);
+                          const int32_t *perm, const int32_t *order,
+                          int64_t n_nodes, int64_t n_edges, int64_t channels,
+                          float *y, float *out, float *norm, void *stream);
 
 /*
  * zs_backward_normalized -- gradients through the normalised scatter (same

@@ -68,14 +68,15 @@ int main(int argc, char **argv)
         return 1;
     }
 
-    void *d_dst, *d_cpl, *d_rad, *d_g, *d_rowptr, *d_perm, *d_dst32, *d_ws, *d_out, *d_gc, *d_gr;
+    void *d_dst, *d_cpl, *d_rad, *d_g, *d_rowptr, *d_perm, *d_dst32, *d_ws, *d_out, *d_gc, *d_gr,
+        *d_order;
     const size_t ws_bytes = zs_csr_workspace_bytes(E, N);
     hipError_t e;
     void **bufs[] = {&d_dst, &d_cpl, &d_rad, &d_g, &d_rowptr, &d_perm, &d_dst32, &d_ws,
-                     &d_out, &d_gc, &d_gr};
+                     &d_out, &d_gc, &d_gr, &d_order};
     const size_t sizes[] = {b_dst, b_cpl, b_rad, b_node, (size_t)(N + 1) * 4, (size_t)E * 4,
-                            (size_t)E * 4, ws_bytes, b_node, b_cpl, b_rad};
-    for (int i = 0; i < 11; ++i)
+                            (size_t)E * 4, ws_bytes, b_node, b_cpl, b_rad, (size_t)N * 4};
+    for (int i = 0; i < 12; ++i)
         if ((e = hipMalloc(bufs[i], sizes[i] ? sizes[i] : 256)) != hipSuccess)
             return fail_hip("hipMalloc", e);
     if ((e = hipMemcpy(d_dst, dst, b_dst, hipMemcpyHostToDevice)) != hipSuccess ||
@@ -84,10 +85,11 @@ int main(int argc, char **argv)
         (e = hipMemcpy(d_g, g, b_node, hipMemcpyHostToDevice)) != hipSuccess)
         return fail_hip("hipMemcpy to device", e);
 
-    int s = zs_build_csr(d_dst, E, N, d_rowptr, d_perm, d_dst32, d_ws, ws_bytes, NULL, NULL);
+    int s = zs_build_csr(d_dst, E, N, d_rowptr, d_perm, d_dst32, d_order, d_ws, ws_bytes, NULL,
+                         NULL);
     if (s != ZS_OK)
         return fail_zs("zs_build_csr", s);
-    s = zs_forward(d_cpl, d_rad, d_rowptr, d_perm, N, E, C, d_out, NULL);
+    s = zs_forward(d_cpl, d_rad, d_rowptr, d_perm, d_order, N, E, C, d_out, NULL);
     if (s != ZS_OK)
         return fail_zs("zs_forward", s);
     s = zs_backward(d_g, d_cpl, d_rad, d_dst32, d_rowptr, d_perm, N, E, C, d_gc, d_gr, NULL);
@@ -115,7 +117,7 @@ int main(int argc, char **argv)
     fwrite(gc, 1, b_cpl, o);
     fwrite(gr, 1, b_rad, o);
     fclose(o);
-    for (int i = 0; i < 11; ++i)
+    for (int i = 0; i < 12; ++i)
         hipFree(*bufs[i]);
     free(dst); free(cpl); free(rad); free(g);
     free(rowptr); free(perm); free(out); free(gc); free(gr);

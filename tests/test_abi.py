@@ -53,8 +53,8 @@ def test_workspace_bytes(lib):
 
 
 def test_build_csr_rejects(lib):
-    def f(dst, e, n, rowptr, perm, dst32, ws, nbytes, flag=None):
-        return lib.zs_build_csr(dst, e, n, rowptr, perm, dst32, ws, nbytes, flag, None)
+    def f(dst, e, n, rowptr, perm, dst32, ws, nbytes, flag=None, order=None):
+        return lib.zs_build_csr(dst, e, n, rowptr, perm, dst32, order, ws, nbytes, flag, None)
     MB = 1 << 20
     assert f(A, 10, 0, B, C_, D, W, MB) == ZS_ERR_SHAPE
     assert f(A, -1, 4, B, C_, D, W, MB) == ZS_ERR_SHAPE
@@ -70,6 +70,10 @@ def test_build_csr_rejects(lib):
     assert f(A, 10, 4, B, C_, D, W + 4, MB) == ZS_ERR_UNSUPPORTED   # workspace alignment
     assert f(A, 10, 4, B, C_, D, A, MB) == ZS_ERR_ALIAS            # workspace over dst
     assert f(A, 10, 4, B, C_, D, W, MB, W + 64) == ZS_ERR_ALIAS     # flag inside workspace
+    assert f(A, 10, 4, B, C_, D, W, MB, None, X + 2) == ZS_ERR_UNSUPPORTED   # order misaligned
+    assert f(A, 10, 4, B, C_, D, W, MB, None, C_ + 8) == ZS_ERR_ALIAS    # order inside perm
+    assert f(A, 10, 4, B, C_, D, W, MB, X, X) == ZS_ERR_ALIAS            # order over flag
+    assert f(A, 10, 4, B, C_, D, W, MB, None, W + 256) == ZS_ERR_ALIAS   # order in workspace
 
 
 def test_noalloc_limit_matches_the_header():
@@ -81,13 +85,14 @@ def test_noalloc_limit_matches_the_header():
 def test_build_csr_noalloc_rejects(lib):
     """The same host checks as zs_build_csr, then the scratch limit: sizes whose
     workspace exceeds the fixed buffer are refused before any HIP call."""
-    def f(dst, e, n, rowptr, perm, dst32, flag=None):
-        return lib.zs_build_csr_noalloc(dst, e, n, rowptr, perm, dst32, flag, None)
+    def f(dst, e, n, rowptr, perm, dst32, flag=None, order=None):
+        return lib.zs_build_csr_noalloc(dst, e, n, rowptr, perm, dst32, order, flag, None)
     assert f(A, 10, 0, B, C_, D) == ZS_ERR_SHAPE
     assert f(None, 10, 4, B, C_, D) == ZS_ERR_NULL
     assert f(A + 4, 10, 4, B, C_, D) == ZS_ERR_UNSUPPORTED
     assert f(A, 10, 4, A + 8, C_, D) == ZS_ERR_ALIAS
     assert f(A, 10, 4, B, C_, D, C_ + 4) == ZS_ERR_ALIAS
+    assert f(A, 10, 4, B, C_, D, None, D + 4) == ZS_ERR_ALIAS     # order inside dst32
     limit = zs.NOALLOC_SCRATCH_BYTES
     assert zs.zs_csr_workspace_bytes(2600000, 16384) <= limit     # the 16384-node frame fits
     big = 5_000_000
@@ -98,15 +103,18 @@ def test_build_csr_noalloc_rejects(lib):
 
 def test_forward_rejects(lib):
     f = lib.zs_forward
-    assert f(A, B, C_, D, 4, 10, 0, X, None) == ZS_ERR_SHAPE
-    assert f(A, B, C_, D, 4, 10, 1025, X, None) == ZS_ERR_SHAPE
-    assert f(A, B, C_, D, 0, 10, 32, X, None) == ZS_ERR_SHAPE
-    assert f(A, B, C_, D, 4, -2, 32, X, None) == ZS_ERR_SHAPE
-    assert f(None, B, C_, D, 4, 10, 32, X, None) == ZS_ERR_NULL
-    assert f(A, B, C_, D, 4, 10, 32, None, None) == ZS_ERR_NULL
-    assert f(A, B + 2, C_, D, 4, 10, 32, X, None) == ZS_ERR_UNSUPPORTED
-    assert f(A, B, C_, D, 4, 10, 32, B + 64, None) == ZS_ERR_ALIAS            # out over radial
-    assert f(A, B, C_, D, 4, 10, 32, A, None) == ZS_ERR_ALIAS                 # out over coupling
+    assert f(A, B, C_, D, None, 4, 10, 0, X, None) == ZS_ERR_SHAPE
+    assert f(A, B, C_, D, None, 4, 10, 1025, X, None) == ZS_ERR_SHAPE
+    assert f(A, B, C_, D, None, 0, 10, 32, X, None) == ZS_ERR_SHAPE
+    assert f(A, B, C_, D, None, 4, -2, 32, X, None) == ZS_ERR_SHAPE
+    assert f(None, B, C_, D, None, 4, 10, 32, X, None) == ZS_ERR_NULL
+    assert f(A, B, C_, D, None, 4, 10, 32, None, None) == ZS_ERR_NULL
+    assert f(A, B + 2, C_, D, None, 4, 10, 32, X, None) == ZS_ERR_UNSUPPORTED
+    assert f(A, B, C_, D, None, 4, 10, 32, B + 64, None) == ZS_ERR_ALIAS            # out over radial
+    assert f(A, B, C_, D, None, 4, 10, 32, A, None) == ZS_ERR_ALIAS                 # out over coupling
+    O = X + (1 << 20)
+    assert f(A, B, C_, D, O + 2, 4, 10, 32, X, None) == ZS_ERR_UNSUPPORTED   # order misaligned
+    assert f(A, B, C_, D, X + 8, 4, 10, 32, X, None) == ZS_ERR_ALIAS         # order inside out
 
 
 def test_backward_rejects(lib):
@@ -125,15 +133,15 @@ def test_backward_rejects(lib):
 
 def test_strided_rejects(lib):
     f, b = lib.zs_forward_strided, lib.zs_backward_strided
-    assert f(A, -1, B, 96, 32, C_, D, 4, 10, 32, X, None) == ZS_ERR_SHAPE      # negative stride
-    assert f(A, 15, B, -96, 32, C_, D, 4, 10, 32, X, None) == ZS_ERR_SHAPE
-    assert f(A, 15, B, 96, -32, C_, D, 4, 10, 32, X, None) == ZS_ERR_SHAPE
-    assert f(A, 46, B, 160, 32, C_, D, 4, 10, 0, X, None) == ZS_ERR_SHAPE      # channels
-    assert f(None, 46, B, 160, 32, C_, D, 4, 10, 32, X, None) == ZS_ERR_NULL
+    assert f(A, -1, B, 96, 32, C_, D, None, 4, 10, 32, X, None) == ZS_ERR_SHAPE      # negative stride
+    assert f(A, 15, B, -96, 32, C_, D, None, 4, 10, 32, X, None) == ZS_ERR_SHAPE
+    assert f(A, 15, B, 96, -32, C_, D, None, 4, 10, 32, X, None) == ZS_ERR_SHAPE
+    assert f(A, 46, B, 160, 32, C_, D, None, 4, 10, 0, X, None) == ZS_ERR_SHAPE      # channels
+    assert f(None, 46, B, 160, 32, C_, D, None, 4, 10, 32, X, None) == ZS_ERR_NULL
     # out inside the strided radial extent (9*160 + 2*32 + 32 floats) -> alias
-    assert f(A, 46, B, 160, 32, C_, D, 4, 10, 32, B + 4 * 1500, None) == ZS_ERR_ALIAS
+    assert f(A, 46, B, 160, 32, C_, D, None, 4, 10, 32, B + 4 * 1500, None) == ZS_ERR_ALIAS
     # out inside the strided coupling extent (9*46 + 15 floats) -> alias
-    assert f(A, 46, B, 160, 32, C_, D, 4, 10, 32, A + 4 * 420, None) == ZS_ERR_ALIAS
+    assert f(A, 46, B, 160, 32, C_, D, None, 4, 10, 32, A + 4 * 420, None) == ZS_ERR_ALIAS
     assert b(A, B, -46, C_, 160, 32, D, D + 4096, D + 8192, 4, 10, 32, W, X, None) == ZS_ERR_SHAPE
     assert b(A, B, 46, C_, 160, 32, D, D + 4096, D + 8192, 4, 10, 32, W, C_ + 4 * 1500,
              None) == ZS_ERR_ALIAS
@@ -141,20 +149,23 @@ def test_strided_rejects(lib):
 
 
 def test_normalized_rejects(lib):
-    # zs_forward_normalized(coupling, radial, env, rowptr, perm, N, E, C, y, out, norm, stream)
+    # zs_forward_normalized(coupling, radial, env, rowptr, perm, order, N, E, C, y, out, norm,
+    #                       stream)
     f = lib.zs_forward_normalized
     Y, O, NR = X, X + (1 << 20), X + (2 << 20)
-    assert f(A, B, W, C_, D, 4, 10, 0, Y, O, NR, None) == ZS_ERR_SHAPE
-    assert f(A, B, None, C_, D, 4, 10, 32, Y, O, NR, None) == ZS_ERR_NULL      # env
-    assert f(A, B, W, C_, D, 4, 10, 32, Y, O, None, None) == ZS_ERR_NULL      # norm
-    assert f(A, B, W, C_, D, 4, 10, 32, None, O, NR, None) == ZS_ERR_NULL     # y
-    assert f(A, B, W + 2, C_, D, 4, 10, 32, Y, O, NR, None) == ZS_ERR_UNSUPPORTED
-    assert f(A, B, W, C_, D, 4, 10, 32, Y, O + 1, NR, None) == ZS_ERR_UNSUPPORTED
-    assert f(A, B, W, C_, D, 4, 10, 32, Y, Y + 64, NR, None) == ZS_ERR_ALIAS  # out over y
-    assert f(A, B, W, C_, D, 4, 10, 32, Y, O, O + 8, None) == ZS_ERR_ALIAS    # norm over out
-    assert f(A, B, W, C_, D, 4, 10, 32, Y, None, Y + 4, None) == ZS_ERR_ALIAS  # norm over y
-    assert f(A, B, W, C_, D, 4, 10, 32, Y, O, W + 4, None) == ZS_ERR_ALIAS    # norm over env
-    assert f(A, B, W, C_, D, 4, 10, 32, B + 64, O, NR, None) == ZS_ERR_ALIAS  # y over radial
+    assert f(A, B, W, C_, D, None, 4, 10, 0, Y, O, NR, None) == ZS_ERR_SHAPE
+    assert f(A, B, None, C_, D, None, 4, 10, 32, Y, O, NR, None) == ZS_ERR_NULL      # env
+    assert f(A, B, W, C_, D, None, 4, 10, 32, Y, O, None, None) == ZS_ERR_NULL      # norm
+    assert f(A, B, W, C_, D, None, 4, 10, 32, None, O, NR, None) == ZS_ERR_NULL     # y
+    assert f(A, B, W + 2, C_, D, None, 4, 10, 32, Y, O, NR, None) == ZS_ERR_UNSUPPORTED
+    assert f(A, B, W, C_, D, None, 4, 10, 32, Y, O + 1, NR, None) == ZS_ERR_UNSUPPORTED
+    assert f(A, B, W, C_, D, None, 4, 10, 32, Y, Y + 64, NR, None) == ZS_ERR_ALIAS  # out over y
+    assert f(A, B, W, C_, D, None, 4, 10, 32, Y, O, O + 8, None) == ZS_ERR_ALIAS    # norm over out
+    assert f(A, B, W, C_, D, None, 4, 10, 32, Y, None, Y + 4, None) == ZS_ERR_ALIAS  # norm over y
+    assert f(A, B, W, C_, D, None, 4, 10, 32, Y, O, W + 4, None) == ZS_ERR_ALIAS    # norm over env
+    assert f(A, B, W, C_, D, None, 4, 10, 32, B + 64, O, NR, None) == ZS_ERR_ALIAS  # y over radial
+    assert f(A, B, W, C_, D, Y + 16, 4, 10, 32, Y, O, NR, None) == ZS_ERR_ALIAS    # order in y
+    assert f(A, B, W, C_, D, X + (5 << 20) + 1, 4, 10, 32, Y, O, NR, None) == ZS_ERR_UNSUPPORTED
     # zs_backward_normalized(gy, out, norm, coupling, radial, dst32, rowptr, perm, N, E, C,
     #                        gc, gr, genv, gdeg, stream)
     b = lib.zs_backward_normalized

@@ -127,6 +127,8 @@ NORM_CASES = [
     ("split_c32", 3000, 200000, 32, "heavy"),
     ("split_c16", 2600, 150000, 16, "heavy"),
     ("split_c8", 2600, 120000, 8, "heavy"),
+    ("heavy_b4_c32", 4096, 300000, 32, "heavy"),    # 4-edge batches, heavy nodes 8-edge
+    ("heavy_b4_c8", 4500, 200000, 8, "heavy"),
     ("split_grid_stride_c8", 1_100_000, 2_300_000, 8, "heavy"),
 ]
 

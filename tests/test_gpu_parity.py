@@ -10,6 +10,10 @@ Bar (all configurations, same seeded inputs on both sides):
 Every workload is compared in full, the large one (E = 2.6M, C = 64) too; it
 also checks the oracle's sampled entry points (used where the full oracle would
 not fit, as for offsets past 2^31) and size-independent properties.
+The node schedule the CSR build also returns (the order in which the forward
+hands out nodes, not a result of the method) is checked against its
+definition in include/zs.h: per-bucket degree ranks laid out rank-major, the
+identity above 16384 nodes.
 """
 import sys
 
@@ -52,7 +56,37 @@ def run_gpu(x, dev, n_nodes):
     gc, gr = zs.zs_backward(g, cpl, rad, csr)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in
-            dict(rowptr=csr.rowptr, perm=csr.perm, dst32=csr.dst32, out=out, gc=gc, gr=gr).items()}
+            dict(rowptr=csr.rowptr, perm=csr.perm, dst32=csr.dst32, order=csr.order, out=out,
+                 gc=gc, gr=gr).items()}
+
+
+def expected_order(rowptr):
+    """The node schedule as include/zs.h defines it: buckets of B consecutive
+    nodes (B the smallest power of two >= N / 256), each ranked by decreasing
+    degree (ties by node id), rank r of full bucket b at r*F + (b + r) mod F
+    (F full buckets), the partial bucket's ranks after them; identity when
+    B > 64."""
+    n = len(rowptr) - 1
+    bn = 1
+    while bn * 256 < n:
+        bn *= 2
+    if bn > 64:
+        return np.arange(n, dtype=np.int32)
+    deg = np.diff(rowptr.astype(np.int64))
+    nf = n // bn
+    order = np.full(n, -1, dtype=np.int64)
+    for b in range(-(-n // bn)):
+        nodes = np.arange(b * bn, min(n, (b + 1) * bn))
+        ranked = nodes[np.lexsort((nodes, -deg[nodes]))]
+        for r, node in enumerate(ranked):
+            order[r * nf + (b + r) % nf if b < nf else nf * bn + r] = node
+    assert np.array_equal(np.sort(order), np.arange(n))
+    return order.astype(np.int32)
+
+
+def check_order(order, rowptr, name):
+    assert np.array_equal(order, expected_order(rowptr)), \
+        f"{name}: node order, {np.count_nonzero(order != expected_order(rowptr))} entries differ"
 
 
 def check_grad_coupling(got, ref, what):
@@ -71,6 +105,8 @@ def compare_full(x, res, n_nodes, name):
     assert np.array_equal(res["rowptr"], rowptr), f"{name}: rowptr"
     assert np.array_equal(res["perm"], perm), f"{name}: perm"
     assert np.array_equal(res["dst32"], x["dst"].astype(np.int32)), f"{name}: dst32"
+    if "order" in res:
+        check_order(res["order"], rowptr, name)
     out = oracle.forward(x["coupling"], x["radial"], x["dst"], n_nodes)
     assert np.array_equal(_bits(res["out"]), _bits(out)), \
         f"{name}: forward, {np.count_nonzero(_bits(res['out']) != _bits(out))} bit differences"
@@ -205,6 +241,16 @@ EDGE_CASES = [
     ("split_c8", 2600, 120000, 8, "heavy"),
     ("split_c4", 2600, 100000, 4, "heavy"),
     ("split_grid_stride_c8", 1_100_000, 2_300_000, 8, "heavy"),
+    # Launches of at least 4096 wavefronts take 4-edge batches, and nodes
+    # above 5/4 of the mean degree 8-edge ones (with the node schedule putting
+    # them first): both paths at each channel width up to 4 per lane.
+    ("heavy_b4_c32", 4096, 300000, 32, "heavy"),
+    ("heavy_b4_c24", 4096, 250000, 24, "heavy"),
+    ("heavy_b4_c16", 4200, 250000, 16, "heavy"),
+    ("heavy_b4_c8", 4500, 200000, 8, "heavy"),
+    ("heavy_b4_c4", 5000, 150000, 4, "heavy"),
+    ("heavy_nodes_20000_c8", 20000, 400000, 8, "heavy"),   # identity schedule above 16384 nodes
+    ("sched_partial_c8", 3333, 120000, 8, "heavy"),     # 16-node buckets, a partial one of 5
 ]
 
 
@@ -247,6 +293,7 @@ def test_no_edges(dev):
     gc, gr = zs.zs_backward(torch.ones((N, 16, C), device=dev), cpl, rad, csr)
     torch.cuda.synchronize()
     assert torch.equal(csr.rowptr.cpu(), torch.zeros(N + 1, dtype=torch.int32))
+    assert torch.equal(csr.order.cpu(), torch.arange(N, dtype=torch.int32))
     assert np.all(_bits(out.cpu().numpy()) == 0)
     assert gc.shape == (0, 15) and gr.shape == (0, 3, C)
 
@@ -342,6 +389,7 @@ def test_csr_only_node_counts(dev, label, N, E):
     assert np.array_equal(csr.rowptr.cpu().numpy(), rowptr), f"{label}: rowptr"
     assert np.array_equal(csr.perm.cpu().numpy(), perm), f"{label}: perm"
     assert np.array_equal(csr.dst32.cpu().numpy(), dst.astype(np.int32)), f"{label}: dst32"
+    check_order(csr.order.cpu().numpy(), rowptr, label)
 
 
 def test_guard_regions_and_unaligned(dev):
@@ -481,7 +529,8 @@ def test_hip_graph_capture_and_replay(dev):
                                                       "grad_out")}
     csr = zs.Csr(torch.empty(N + 1, dtype=torch.int32, device=dev),
                  torch.empty(E, dtype=torch.int32, device=dev),
-                 torch.empty(E, dtype=torch.int32, device=dev), N)
+                 torch.empty(E, dtype=torch.int32, device=dev), N,
+                 torch.empty(N, dtype=torch.int32, device=dev))
     ws = torch.empty(zs.zs_csr_workspace_bytes(E, N), dtype=torch.uint8, device=dev)
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     out = torch.empty((N, 16, C), device=dev)
@@ -495,10 +544,10 @@ def test_hip_graph_capture_and_replay(dev):
                        grad_radial=gr)
         y, o, nrm = zs.zs_forward_normalized(t["coupling"], t["radial"], t["env"], csr)
         grads = zs.zs_backward_normalized(t["grad_out"], o, nrm, t["coupling"], t["radial"], csr)
-        return [csr.rowptr, csr.perm, csr.dst32, out, gc, gr, y, o, nrm, *grads]
+        return [csr.rowptr, csr.perm, csr.dst32, csr.order, out, gc, gr, y, o, nrm, *grads]
 
-    names = ("rowptr", "perm", "dst32", "out", "gc", "gr", "y", "out_n", "norm", "gc_n", "gr_n",
-             "genv", "gdeg")
+    names = ("rowptr", "perm", "dst32", "order", "out", "gc", "gr", "y", "out_n", "norm", "gc_n",
+             "gr_n", "genv", "gdeg")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -521,3 +570,36 @@ def test_hip_graph_capture_and_replay(dev):
         assert int(flag.item()) == 0
     ref_out = oracle.forward(x["coupling"], x["radial"], x["dst"], N)
     assert np.array_equal(_bits(out.cpu().numpy()), _bits(ref_out))
+
+
+def test_node_order_is_a_schedule_only(dev):
+    """The forward with the node order, without it (NULL), and with an order
+    whose entries are partly not nodes: the first two are bitwise equal to the
+    oracle; the third skips the positions that hold no node (range-checked, no
+    access outside the buffers) and leaves those nodes' rows as they were."""
+    N, E, C = 4096, 300000, 32
+    w = synthetic.custom("order_sched", N, E, C, seed=6061, envelope=True)
+    x = synthetic.make_inputs(w, with_grad=False)
+    x["dst"] = heavy_destinations(E, N, seed=6061)
+    say(f"[gpu] node order as a schedule: N={N} E={E} C={C}")
+    dst = torch.from_numpy(x["dst"]).to(dev)
+    cpl = torch.from_numpy(x["coupling"]).to(dev)
+    rad = torch.from_numpy(x["radial"]).to(dev)
+    csr = zs.zs_build_csr(dst, N)
+    with_order = zs.zs_forward(cpl, rad, csr)
+    without = zs.zs_forward(cpl, rad, csr._replace(order=None))
+    bad = csr.order.clone()
+    dropped = bad[:6].clone()                       # six of the highest-degree nodes
+    bad[:3] = -1
+    bad[3:6] = N + 3
+    partial = zs.zs_forward(cpl, rad, csr._replace(order=bad),
+                            out=torch.full((N, 16, C), float("nan"), device=dev))
+    torch.cuda.synchronize()
+    ref = oracle.forward(x["coupling"], x["radial"], x["dst"], N)
+    assert np.array_equal(_bits(with_order.cpu().numpy()), _bits(ref))
+    assert np.array_equal(_bits(without.cpu().numpy()), _bits(ref))
+    got = partial.cpu().numpy()
+    skip = np.zeros(N, dtype=bool)
+    skip[dropped.cpu().numpy()] = True
+    assert np.all(np.isnan(got[skip]))
+    assert np.array_equal(_bits(got[~skip]), _bits(ref[~skip]))

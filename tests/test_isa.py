@@ -59,7 +59,11 @@ def test_no_fp32_fma_or_packed_ops(asm):
             seen += 1
             body, nb = _strip_sqrt_div(body)
             normalised = "zs_fwd" in sym and sym.split("NS_8InLayout")[0].endswith("Lb1EEEvPKfS3_")
-            assert nb == (1 if normalised else 0), sym
+            # the staged kernel's 4-edge instantiations at <= 4 channels per lane
+            # also hold the 8-edge path for heavy nodes: one block per path
+            m = re.search(r"zs_fwd_staged_kernelILi(\d+)ELi(\d+)E", sym)
+            paths = 2 if m and int(m.group(1)) <= 4 and int(m.group(2)) == 4 else 1
+            assert nb == (paths if normalised else 0), sym
             norm_blocks += nb
             bad = re.findall(r"\b(v_fmac?_f32|v_fma_mix\w*|v_pk_(?:fma|mul|add)_f32|v_mad_f32)\b",
                              body)

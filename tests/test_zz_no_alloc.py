@@ -30,11 +30,12 @@ def dev():
 def _empty_csr(n_nodes, n_edges, dev, fill):
     return zs.Csr(torch.full((n_nodes + 1,), fill, dtype=torch.int32, device=dev),
                   torch.full((n_edges,), fill, dtype=torch.int32, device=dev),
-                  torch.full((n_edges,), fill, dtype=torch.int32, device=dev), n_nodes)
+                  torch.full((n_edges,), fill, dtype=torch.int32, device=dev), n_nodes,
+                  torch.full((n_nodes,), fill, dtype=torch.int32, device=dev))
 
 
 def _same(a: zs.Csr, b: zs.Csr, what: str):
-    for name in ("rowptr", "perm", "dst32"):
+    for name in ("rowptr", "perm", "dst32", "order"):
         x, y = getattr(a, name).cpu().numpy(), getattr(b, name).cpu().numpy()
         assert np.array_equal(x, y), f"{what}: {name} differs"
 
