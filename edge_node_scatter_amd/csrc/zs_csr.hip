@@ -87,13 +87,16 @@ __global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
         p[i] = v;
 }
 
+// Inclusive scan over the wavefront with DPP lane moves: shifts by 1, 2, 4
+// and 8 inside each 16-lane row (lanes past the row's start read 0), then
+// row 0's and row 1's last lanes broadcast into the rows above them.
 __device__ inline int32_t wave_inclusive_scan(int32_t v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int32_t u = __shfl_up(v, d, 64);
-        if (lane >= d) v += u;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
     return v;
 }
 
@@ -116,11 +119,11 @@ __device__ inline int32_t block_exclusive_scan_lds(int32_t* a, int64_t n) {
     const int wave = tid >> 6, lane = tid & 63;
     if (lane == 63) wave_tot[wave] = incl;
     __syncthreads();
-    int32_t off = 0, total = 0;
-    for (int w = 0; w < TH / 64; ++w) {
-        if (w < wave) off += wave_tot[w];
-        total += wave_tot[w];
-    }
+    // every lane reads one wavefront total; their scan gives each wavefront
+    // its offset (entry wave - 1) and the total (entry TH/64 - 1)
+    const int32_t tots = wave_inclusive_scan(lane < TH / 64 ? wave_tot[lane] : 0);
+    const int32_t total = __builtin_amdgcn_readlane(tots, TH / 64 - 1);
+    int32_t off = wave > 0 ? __builtin_amdgcn_readlane(tots, wave - 1) : 0;
     off += incl - local;
     for (int64_t i = lo; i < hi; ++i) a[i] += off;
     __syncthreads();
@@ -301,6 +304,37 @@ struct BucketRuns {
     int64_t chunk_edges;
     const int2* pairs;
 
+    // Pairs at K sequence indices at once; only the first nv (uniform over
+    // the wavefront) are looked up, and entries with ok[k] false get
+    // (-1, -1).  Binary lifting from chunk 0 by the powers of two from top
+    // (the largest one below chunks) down, the indices stepping together so
+    // that the LDS reads of a step are in flight at the same time.  Finds,
+    // like at(), the largest c with runpre[c] <= i (runs are < 2^31 long).
+    template <int K>
+    __device__ __attribute__((always_inline)) void at_k(const int64_t (&i)[K], const bool (&ok)[K],
+                                                        int nv, int32_t top, int2 (&out)[K]) const {
+        int32_t c[K], ii[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            c[k] = 0;
+            ii[k] = int32_t(i[k]);
+        }
+        const int32_t nch = int32_t(chunks);
+        for (int32_t step = top; step > 0; step >>= 1) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                if (k >= nv) break;   // uniform
+                const int32_t cand = c[k] + step;
+                if (cand < nch && runpre[cand] <= ii[k]) c[k] = cand;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            out[k] = k < nv && ok[k]
+                         ? pairs[int64_t(c[k]) * chunk_edges + runoff[c[k]] + (ii[k] - runpre[c[k]])]
+                         : make_int2(-1, -1);
+    }
+
     // pair at sequence index i (0 <= i < runpre[W])
     __device__ __attribute__((always_inline)) int2 at(int64_t i) const {
         int64_t lo = 0, hi = chunks - 1;      // largest c with runpre[c] <= i
@@ -371,13 +405,19 @@ __global__ __launch_bounds__(kThreads) void csr_bucket_place_kernel(
     const int64_t p1 = p0 + part < size ? p0 + part : size;
 
     const bool single = p1 - p0 <= 64 * kAhead;
+    int32_t top = 0;   // largest power of two below chunks (0 for one chunk)
+    while (chunks > 1 && int64_t(top) * 2 < chunks) top = top ? top * 2 : 1;
     int2 pr[kAhead];
     auto load = [&](int64_t at) {
+        int64_t idx[kAhead];
+        bool ok[kAhead];
 #pragma unroll
         for (int j = 0; j < kAhead; ++j) {
-            const int64_t i = at + j * 64 + lane;
-            pr[j] = i < p1 ? seq.at(i) : make_int2(-1, -1);
+            idx[j] = at + j * 64 + lane;
+            ok[j] = idx[j] < p1;
         }
+        const int64_t left = (p1 - at + 63) / 64;
+        seq.at_k<kAhead>(idx, ok, int(left < kAhead ? left : kAhead), top, pr);
     };
     for (int64_t at = p0; at < p1; at += 64 * kAhead) {
         load(at);
