@@ -19,6 +19,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "zs_oracle.c")
 _LIB = os.path.join(_HERE, "libzs_oracle.so")
+_SRC_MT = os.path.join(_HERE, "zs_oracle_mt.c")
+_LIB_MT = os.path.join(_HERE, "libzs_oracle_mt.so")
 
 GCC_FLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-fno-builtin-sqrt",
              "-fno-fast-math", "-fexcess-precision=standard", "-Wall", "-Werror"]
@@ -31,6 +33,17 @@ def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
         subprocess.check_call(["gcc", *GCC_FLAGS, src, "-o", tmp, "-lm"])
         os.replace(tmp, out)
     return out
+
+
+def build_mt(force: bool = True) -> str:
+    """Compile the K-thread variant (zs_oracle_mt.c, which includes
+    zs_oracle.c) with gcc -fopenmp."""
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_SRC_MT))
+    if force or not os.path.exists(_LIB_MT) or os.path.getmtime(_LIB_MT) < newest:
+        tmp = _LIB_MT + ".tmp"
+        subprocess.check_call(["gcc", *GCC_FLAGS, "-fopenmp", _SRC_MT, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_MT)
+    return _LIB_MT
 
 
 _SIGS = {
@@ -210,3 +223,52 @@ def forward_norm(*a, **k):
 
 def backward_norm(*a, **k):
     return get().backward_norm(*a, **k)
+
+
+class OracleMT:
+    """The K-thread variant: node-blocked forward (each node's edges in
+    increasing edge id, from the oracle's CSR) and edge-blocked backward,
+    bitwise equal to the oracle's forward and backward."""
+
+    def __init__(self, libpath: str):
+        lib = ctypes.CDLL(libpath)
+        for name, sig in {"zs_oracle_mt_forward_f32": "PPPPIIPI",
+                          "zs_oracle_mt_backward_f32": "PPPPIIIPPI"}.items():
+            fn = getattr(lib, name)
+            fn.argtypes = [ctypes.c_void_p if ch == "P" else ctypes.c_int64 for ch in sig]
+            fn.restype = ctypes.c_int
+        self.lib = lib
+
+    def forward(self, coupling, radial, dst, n_nodes, threads, csr=None):
+        dst, coupling, radial, E, C = _prep(dst, coupling, radial)
+        rowptr, perm = csr if csr is not None else get().csr(dst, n_nodes)
+        rowptr = np.ascontiguousarray(rowptr, dtype=np.int32)
+        perm = np.ascontiguousarray(perm, dtype=np.int32)
+        out = np.empty((n_nodes, 16, C), dtype=np.float32)
+        _check(self.lib.zs_oracle_mt_forward_f32(_p(coupling), _p(radial), _p(rowptr), _p(perm),
+                                                 n_nodes, C, _p(out), threads))
+        return out
+
+    def backward(self, grad_out, coupling, radial, dst, threads):
+        dst, coupling, radial, E, C = _prep(dst, coupling, radial)
+        grad_out = np.ascontiguousarray(grad_out, dtype=np.float32)
+        N = grad_out.shape[0]
+        if grad_out.shape != (N, 16, C):
+            raise ValueError("bad grad_out shape")
+        gc = np.empty((E, 15), dtype=np.float32)
+        gr = np.empty((E, 3, C), dtype=np.float32)
+        _check(self.lib.zs_oracle_mt_backward_f32(_p(grad_out), _p(coupling), _p(radial), _p(dst),
+                                                  E, N, C, _p(gc), _p(gr), threads))
+        return gc, gr
+
+
+_default_mt = None
+
+
+def get_mt() -> OracleMT:
+    """The K-thread variant built from the committed sources."""
+    global _default_mt
+    if _default_mt is None:
+        build_mt(force=False)
+        _default_mt = OracleMT(_LIB_MT)
+    return _default_mt
