@@ -151,17 +151,19 @@ int zs_build_csr_noalloc(const int64_t *dst, int64_t n_edges, int64_t n_nodes,
  *                                            index order).  It decides only which
  *                                            wavefront sums which node and when
  *                                            (every bucket's highest-degree nodes
- *                                            first, spread over the compute units);
- *                                            out is bitwise the same.
+ *                                            first, spread over the compute units):
+ *                                            any permutation of 0..n_nodes-1 gives
+ *                                            bitwise the same out.
  *   out      [n_nodes][16][channels]   fp32  fully overwritten (output)
  *
  * out[n][0][:] = +0; out[n][r][c] adds fp32(coupling*radial) products over the
  * node's edges in increasing edge id, starting from +0, with separate fp32
  * multiply and add (no fused multiply-add): bitwise the fp32 result of the
  * materialised message followed by index_add.  Run-to-run deterministic.
- * A CSR or order that zs_build_csr did not produce gives unspecified values
- * but no out-of-bounds access (positions, edge ids and order entries are
- * range-checked).
+ * A CSR that zs_build_csr did not produce gives unspecified values but no
+ * out-of-bounds access (positions and edge ids are range-checked); an order
+ * entry outside [0, n_nodes) is skipped, so the nodes such an order leaves
+ * out keep their previous out rows.
  */
 int zs_forward(const float *coupling, const float *radial,
                const int32_t *rowptr, const int32_t *perm, const int32_t *order,

@@ -573,10 +573,11 @@ def test_hip_graph_capture_and_replay(dev):
 
 
 def test_node_order_is_a_schedule_only(dev):
-    """The forward with the node order, without it (NULL), and with an order
-    whose entries are partly not nodes: the first two are bitwise equal to the
-    oracle; the third skips the positions that hold no node (range-checked, no
-    access outside the buffers) and leaves those nodes' rows as they were."""
+    """The forward with the node schedule, without it (NULL), with a random
+    permutation of the nodes, and with an order whose entries are partly not
+    nodes: the first three are bitwise equal to the oracle; the last skips the
+    positions that hold no node (range-checked, no access outside the
+    buffers) and leaves those nodes' rows as they were."""
     N, E, C = 4096, 300000, 32
     w = synthetic.custom("order_sched", N, E, C, seed=6061, envelope=True)
     x = synthetic.make_inputs(w, with_grad=False)
@@ -588,6 +589,8 @@ def test_node_order_is_a_schedule_only(dev):
     csr = zs.zs_build_csr(dst, N)
     with_order = zs.zs_forward(cpl, rad, csr)
     without = zs.zs_forward(cpl, rad, csr._replace(order=None))
+    shuffled = torch.from_numpy(np.random.default_rng(6062).permutation(N).astype(np.int32)).to(dev)
+    any_perm = zs.zs_forward(cpl, rad, csr._replace(order=shuffled))
     bad = csr.order.clone()
     dropped = bad[:6].clone()                       # six of the highest-degree nodes
     bad[:3] = -1
@@ -598,6 +601,7 @@ def test_node_order_is_a_schedule_only(dev):
     ref = oracle.forward(x["coupling"], x["radial"], x["dst"], N)
     assert np.array_equal(_bits(with_order.cpu().numpy()), _bits(ref))
     assert np.array_equal(_bits(without.cpu().numpy()), _bits(ref))
+    assert np.array_equal(_bits(any_perm.cpu().numpy()), _bits(ref))
     got = partial.cpu().numpy()
     skip = np.zeros(N, dtype=bool)
     skip[dropped.cpu().numpy()] = True
