@@ -418,7 +418,9 @@ def copy_probe(torch, dev, reps: int = 10) -> dict:
             "note": "torch device copy of 256 MiB (read + write), median of 10"}
 
 
-WORKLOADS_REPORTED = ("n1000", "skewed", "large")
+# the other frames, and the headline shape with i.i.d. uniform destinations
+# (Poisson degrees) as a secondary row of the headline
+WORKLOADS_REPORTED = ("n1000", "skewed", "large", "headline_uniform")
 
 
 def progress(msg: str) -> None:
