@@ -514,18 +514,25 @@ constexpr uint32_t kBwdPartEdges = ZS_BWD_PART_EDGES;
 // several XCDs).
 constexpr int64_t kBwdPartShift = 8;
 
-// floor(len * p / parts) for parts in 1..kBwdMaxParts, as 32-bit divisions by
-// constants.
+// Start of part p of a node's len edges split into `parts` (p = parts: len):
+// floor(len * p / parts), for interior points rounded to the nearest multiple
+// of STEP (the edges one step of the wavefront takes), so that only a node's
+// last part ends with a partly filled step.  32-bit divisions by constants.
+template <uint32_t STEP>
 __device__ __attribute__((always_inline)) inline uint32_t split_point(uint32_t len, uint32_t p,
                                                                       uint32_t parts) {
+    if (p == 0) return 0;
+    if (p >= parts) return len;
     const uint64_t x = uint64_t(len) * p;
+    uint32_t at;
     switch (parts) {
-        case 1: return uint32_t(x);
-        case 2: return uint32_t(x / 2);
-        case 3: return uint32_t(x / 3);
-        case 4: return uint32_t(x / 4);
-        default: return uint32_t(x / parts);
+        case 2: at = uint32_t(x / 2); break;
+        case 3: at = uint32_t(x / 3); break;
+        case 4: at = uint32_t(x / 4); break;
+        default: at = uint32_t(x / parts); break;
     }
+    at = (at + STEP / 2) / STEP * STEP;
+    return at < len ? at : len;
 }
 
 // FULL: C == NQ*VEC, every lane holds real channels (no channel masking).
@@ -578,8 +585,8 @@ void zs_bwd_staged_kernel(
             parts = parts < 1 ? 1 : (parts > kBwdMaxParts ? kBwdMaxParts : parts);
             if (uint32_t(part) >= parts) continue;
             const int64_t base = k0;
-            k0 = base + split_point(len, uint32_t(part), parts);
-            k1 = base + split_point(len, uint32_t(part) + 1, parts);
+            k0 = base + split_point<EPW>(len, uint32_t(part), parts);
+            k1 = base + split_point<EPW>(len, uint32_t(part) + 1, parts);
         }
         const bool deg = ng.grad_deg != nullptr && part == 0;   // also form the degree gradient
         if (k0 >= k1 && !deg) continue;
