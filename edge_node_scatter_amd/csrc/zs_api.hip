@@ -177,24 +177,39 @@ int zs_build_csr_noalloc(const int64_t* dst, int64_t n_edges, int64_t n_nodes,
 
 namespace {
 
-// Strided input layouts: any non-negative strides (inputs are only read, so
-// overlapping or broadcast rows are harmless).
-bool layout_ok(int64_t cs, int64_t re, int64_t rs, int64_t C) {
-    (void)C;
-    return cs >= 0 && re >= 0 && rs >= 0;
+// Largest extent, in floats, of a strided input view (2^60: the view's byte
+// extent and every index the kernels form stay far inside int64).
+constexpr int64_t kMaxExtent = int64_t(1) << 60;
+
+// Floats spanned by E edges of the strided inputs, or -1 when that extent
+// overflows or exceeds kMaxExtent.
+int64_t view_extent(int64_t E, int64_t edge_stride, int64_t tail) {
+    if (E <= 0) return 0;
+    int64_t x = 0;
+    if (__builtin_mul_overflow(E - 1, edge_stride, &x) || __builtin_add_overflow(x, tail, &x) ||
+        x > kMaxExtent)
+        return -1;
+    return x;
+}
+int64_t cpl_extent(int64_t E, int64_t cs) { return view_extent(E, cs, zs::kZonal); }
+int64_t rad_extent(int64_t E, int64_t re, int64_t rs, int64_t C) {
+    if (rs > kMaxExtent) return -1;
+    return view_extent(E, re, 2 * rs + C);
 }
 
-// Floats spanned by E edges of the strided inputs.
-int64_t cpl_extent(int64_t E, int64_t cs) { return E > 0 ? (E - 1) * cs + zs::kZonal : 0; }
-int64_t rad_extent(int64_t E, int64_t re, int64_t rs, int64_t C) {
-    return E > 0 ? (E - 1) * re + 2 * rs + C : 0;
+// Strided input layouts: any non-negative strides (inputs are only read, so
+// overlapping or broadcast rows are harmless) whose views span at most
+// kMaxExtent floats.
+bool layout_ok(int64_t E, int64_t cs, int64_t re, int64_t rs, int64_t C) {
+    return cs >= 0 && re >= 0 && rs >= 0 && cpl_extent(E, cs) >= 0 &&
+           rad_extent(E, re, rs, C) >= 0;
 }
 
 int forward_impl(const float* coupling, int64_t cs, const float* radial, int64_t re, int64_t rs,
                  const int32_t* rowptr, const int32_t* perm, const int32_t* order,
                  int64_t n_nodes, int64_t n_edges, int64_t channels, float* out, void* stream) {
     if (!sizes_ok(n_edges, n_nodes) || !channels_ok(channels)) return ZS_ERR_SHAPE;
-    if (!layout_ok(cs, re, rs, channels)) return ZS_ERR_SHAPE;
+    if (!layout_ok(n_edges, cs, re, rs, channels)) return ZS_ERR_SHAPE;
     if (!out || !rowptr || (n_edges > 0 && (!coupling || !radial || !perm))) return ZS_ERR_NULL;
     if (!aligned(out, 4) || !aligned(rowptr, 4) || (order && !aligned(order, 4)) ||
         (n_edges > 0 && (!aligned(coupling, 4) || !aligned(radial, 4) || !aligned(perm, 4))))
@@ -218,7 +233,7 @@ int backward_impl(const float* grad_out, const float* coupling, int64_t cs, cons
                   const int32_t* perm, int64_t n_nodes, int64_t n_edges, int64_t channels,
                   float* grad_coupling, float* grad_radial, void* stream) {
     if (!sizes_ok(n_edges, n_nodes) || !channels_ok(channels)) return ZS_ERR_SHAPE;
-    if (!layout_ok(cs, re, rs, channels)) return ZS_ERR_SHAPE;
+    if (!layout_ok(n_edges, cs, re, rs, channels)) return ZS_ERR_SHAPE;
     if (n_edges == 0) return ZS_OK;   // both gradients are empty
     if (!grad_out || !coupling || !radial || !dst32 || !rowptr || !perm || !grad_coupling ||
         !grad_radial)

@@ -214,8 +214,10 @@ int zs_backward(const float *grad_out, const float *coupling,
  *   radial[e][s][c]  is read at radial[e * radial_edge_stride +
  *                                      s * radial_slot_stride + c]
  *
- * Strides are in floats and must be >= 0 (else ZS_ERR_SHAPE); inputs are
- * only read, so overlapping or broadcast (stride 0) rows are allowed.  Outputs
+ * Strides are in floats and must be >= 0, with each view spanning at most
+ * 2^60 floats ((n_edges - 1) * edge stride plus its last row), else
+ * ZS_ERR_SHAPE; inputs are only read, so overlapping or broadcast (stride 0)
+ * rows are allowed.  Outputs
  * are contiguous as in zs_forward/zs_backward, must not overlap the strided
  * inputs' extents, and results are identical to those calls on contiguous
  * copies of the views.

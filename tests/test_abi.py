@@ -137,6 +137,13 @@ def test_strided_rejects(lib):
     assert f(A, 15, B, -96, 32, C_, D, None, 4, 10, 32, X, None) == ZS_ERR_SHAPE
     assert f(A, 15, B, 96, -32, C_, D, None, 4, 10, 32, X, None) == ZS_ERR_SHAPE
     assert f(A, 46, B, 160, 32, C_, D, None, 4, 10, 0, X, None) == ZS_ERR_SHAPE      # channels
+    # views whose extent overflows int64 or passes 2^60 floats
+    big = 1 << 62
+    assert f(A, big, B, 96, 32, C_, D, None, 4, 10, 32, X, None) == ZS_ERR_SHAPE
+    assert f(A, 15, B, big, 32, C_, D, None, 4, 10, 32, X, None) == ZS_ERR_SHAPE
+    assert f(A, 15, B, 96, big, C_, D, None, 4, 10, 32, X, None) == ZS_ERR_SHAPE
+    assert f(A, (1 << 60) // 9 + 1, B, 96, 32, C_, D, None, 4, 10, 32, X, None) == ZS_ERR_SHAPE
+    assert b(A, B, 46, C_, big, 32, D, D + 4096, D + 8192, 4, 10, 32, W, X, None) == ZS_ERR_SHAPE
     assert f(None, 46, B, 160, 32, C_, D, None, 4, 10, 32, X, None) == ZS_ERR_NULL
     # out inside the strided radial extent (9*160 + 2*32 + 32 floats) -> alias
     assert f(A, 46, B, 160, 32, C_, D, None, 4, 10, 32, B + 4 * 1500, None) == ZS_ERR_ALIAS
