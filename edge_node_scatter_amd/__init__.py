@@ -105,8 +105,12 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _stream() -> int:
-    return torch.cuda.current_stream().cuda_stream
+def _call(dev: torch.device, fn, *args) -> int:
+    """One library call with ``dev`` as the current device and its current
+    stream as the last argument (the library launches on the current device
+    and keeps its no-allocation scratch per device)."""
+    with torch.cuda.device(dev):
+        return fn(*args, torch.cuda.current_stream(dev).cuda_stream)
 
 
 def _dev_tensor(t: torch.Tensor, name: str, dtype: torch.dtype,
@@ -218,9 +222,9 @@ def zs_build_csr(dst: torch.Tensor, n_nodes: int, workspace: torch.Tensor | None
         _buffer(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
     if bad_flag is not None:
         _buffer(bad_flag, "bad_flag", (1,), torch.int32, dev)
-    _check("zs_build_csr", load().zs_build_csr(
-        _ptr(dst), E, n_nodes, _ptr(out.rowptr), _ptr(out.perm), _ptr(out.dst32), _ptr(out.order),
-        _ptr(workspace), workspace.numel(), _ptr(bad_flag), _stream()))
+    _check("zs_build_csr", _call(
+        dev, load().zs_build_csr, _ptr(dst), E, n_nodes, _ptr(out.rowptr), _ptr(out.perm),
+        _ptr(out.dst32), _ptr(out.order), _ptr(workspace), workspace.numel(), _ptr(bad_flag)))
     return out
 
 
@@ -238,14 +242,15 @@ def zs_build_csr_noalloc(dst: torch.Tensor, n_nodes: int, out: Csr,
     if not dst.is_contiguous():
         raise ValueError("dst must be contiguous")
     E = dst.numel()
+    dev = dst.device
     if out.n_nodes != n_nodes:
         raise ValueError(f"out.n_nodes is {out.n_nodes}, expected {n_nodes}")
-    _csr_buffers(out, E, dst.device)
+    _csr_buffers(out, E, dev)
     if bad_flag is not None:
-        _buffer(bad_flag, "bad_flag", (1,), torch.int32, dst.device)
-    _check("zs_build_csr_noalloc", load().zs_build_csr_noalloc(
-        _ptr(dst), E, n_nodes, _ptr(out.rowptr), _ptr(out.perm), _ptr(out.dst32), _ptr(out.order),
-        _ptr(bad_flag), _stream()))
+        _buffer(bad_flag, "bad_flag", (1,), torch.int32, dev)
+    _check("zs_build_csr_noalloc", _call(
+        dev, load().zs_build_csr_noalloc, _ptr(dst), E, n_nodes, _ptr(out.rowptr),
+        _ptr(out.perm), _ptr(out.dst32), _ptr(out.order), _ptr(bad_flag)))
     return out
 
 
@@ -266,12 +271,12 @@ def zs_forward(coupling: torch.Tensor, radial: torch.Tensor, csr: Csr,
     else:
         _buffer(out, "out", (csr.n_nodes, ROWS, C), torch.float32, dev)
     if coupling.is_contiguous() and radial.is_contiguous():
-        status = load().zs_forward(_ptr(coupling), _ptr(radial), _ptr(csr.rowptr), _ptr(csr.perm),
-                                   _ptr(csr.order), csr.n_nodes, E, C, _ptr(out), _stream())
+        status = _call(dev, load().zs_forward, _ptr(coupling), _ptr(radial), _ptr(csr.rowptr),
+                       _ptr(csr.perm), _ptr(csr.order), csr.n_nodes, E, C, _ptr(out))
     else:
-        status = load().zs_forward_strided(_ptr(coupling), cs, _ptr(radial), re, rs,
-                                           _ptr(csr.rowptr), _ptr(csr.perm), _ptr(csr.order),
-                                           csr.n_nodes, E, C, _ptr(out), _stream())
+        status = _call(dev, load().zs_forward_strided, _ptr(coupling), cs, _ptr(radial), re, rs,
+                       _ptr(csr.rowptr), _ptr(csr.perm), _ptr(csr.order), csr.n_nodes, E, C,
+                       _ptr(out))
     _check("zs_forward", status)
     return out
 
@@ -300,14 +305,13 @@ def zs_backward(grad_out: torch.Tensor, coupling: torch.Tensor, radial: torch.Te
     else:
         _buffer(grad_radial, "grad_radial", (E, SLOTS, C), torch.float32, dev)
     if coupling.is_contiguous() and radial.is_contiguous():
-        status = load().zs_backward(_ptr(grad_out), _ptr(coupling), _ptr(radial), _ptr(csr.dst32),
-                                    _ptr(csr.rowptr), _ptr(csr.perm), csr.n_nodes, E, C,
-                                    _ptr(grad_coupling), _ptr(grad_radial), _stream())
+        status = _call(dev, load().zs_backward, _ptr(grad_out), _ptr(coupling), _ptr(radial),
+                       _ptr(csr.dst32), _ptr(csr.rowptr), _ptr(csr.perm), csr.n_nodes, E, C,
+                       _ptr(grad_coupling), _ptr(grad_radial))
     else:
-        status = load().zs_backward_strided(_ptr(grad_out), _ptr(coupling), cs, _ptr(radial), re,
-                                            rs, _ptr(csr.dst32), _ptr(csr.rowptr), _ptr(csr.perm),
-                                            csr.n_nodes, E, C, _ptr(grad_coupling),
-                                            _ptr(grad_radial), _stream())
+        status = _call(dev, load().zs_backward_strided, _ptr(grad_out), _ptr(coupling), cs,
+                       _ptr(radial), re, rs, _ptr(csr.dst32), _ptr(csr.rowptr), _ptr(csr.perm),
+                       csr.n_nodes, E, C, _ptr(grad_coupling), _ptr(grad_radial))
     _check("zs_backward", status)
     return grad_coupling, grad_radial
 
@@ -339,9 +343,10 @@ def zs_forward_normalized(coupling: torch.Tensor, radial: torch.Tensor, env: tor
     y = torch.empty((csr.n_nodes, ROWS, C), dtype=torch.float32, device=dev)
     out = torch.empty_like(y) if keep_out else None
     norm = torch.empty(csr.n_nodes, dtype=torch.float32, device=dev)
-    _check("zs_forward_normalized", load().zs_forward_normalized(
-        _ptr(coupling), _ptr(radial), _ptr(env), _ptr(csr.rowptr), _ptr(csr.perm),
-        _ptr(csr.order), csr.n_nodes, E, C, _ptr(y), _ptr(out), _ptr(norm), _stream()))
+    _check("zs_forward_normalized", _call(
+        dev, load().zs_forward_normalized, _ptr(coupling), _ptr(radial), _ptr(env),
+        _ptr(csr.rowptr), _ptr(csr.perm), _ptr(csr.order), csr.n_nodes, E, C, _ptr(y), _ptr(out),
+        _ptr(norm)))
     return y, out, norm
 
 
@@ -366,10 +371,10 @@ def zs_backward_normalized(grad_y: torch.Tensor, out: torch.Tensor, norm: torch.
     gr = torch.empty((E, SLOTS, C), dtype=torch.float32, device=dev)
     ge = torch.empty(E, dtype=torch.float32, device=dev)
     gd = torch.empty(N, dtype=torch.float32, device=dev)
-    _check("zs_backward_normalized", load().zs_backward_normalized(
-        _ptr(grad_y), _ptr(out), _ptr(norm), _ptr(coupling), _ptr(radial), _ptr(csr.dst32),
-        _ptr(csr.rowptr), _ptr(csr.perm), N, E, C, _ptr(gc), _ptr(gr), _ptr(ge), _ptr(gd),
-        _stream()))
+    _check("zs_backward_normalized", _call(
+        dev, load().zs_backward_normalized, _ptr(grad_y), _ptr(out), _ptr(norm), _ptr(coupling),
+        _ptr(radial), _ptr(csr.dst32), _ptr(csr.rowptr), _ptr(csr.perm), N, E, C, _ptr(gc),
+        _ptr(gr), _ptr(ge), _ptr(gd)))
     return gc, gr, ge, gd
 
 
