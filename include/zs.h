@@ -17,12 +17,15 @@
  *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers owned by the caller.  The library
- *    never allocates, frees or retains them, and keeps no global state.
+ *    never allocates, frees or retains them, and keeps no global state apart
+ *    from zs_build_csr_noalloc's fixed per-device scratch (below).
+ *  - Kernels run on the calling thread's current HIP device; every buffer and
+ *    the stream must belong to that device.
  *  - Arrays are dense, row-major and contiguous; fp32 arrays must be 4-byte
  *    aligned (16-byte alignment and C % 4 == 0 select the vector kernels).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
- *    stream), except zs_build_csr without a bad_flag, which synchronizes
- *    `stream` once at the end to read back its index-validation flag.
+ *    stream), except the CSR builds without a bad_flag, which synchronize
+ *    `stream` once at the end to read back their index-validation flag.
  *  - Inputs are never written.  Outputs must not overlap inputs or each other.
  *  - Sizes: 0 <= n_edges <= ZS_MAX_EDGES, 1 <= n_nodes <= ZS_MAX_NODES,
  *    1 <= channels <= ZS_MAX_CHANNELS.  n_edges == 0 is valid.
