@@ -430,10 +430,12 @@ def progress(msg: str) -> None:
 
 def time_workloads(zs, torch, dev, names, steps: int) -> dict:
     """Warm and cache-flushed forward + backward of other frames, in this
-    process after the headline's timed region: per frame, the CSR build once,
-    a few warmup passes, then ``steps`` back-to-back passes with an event
-    around each call (warm) and ``min(steps, 20)`` samples each preceded by
-    the read flush (flushed).  Inputs are freed before the next frame."""
+    process after the headline's timed region.  Every pass is a step shaped
+    like the headline's: CSR build, forward, backward, with an event around
+    the forward and the backward (the build is not timed); per frame a few
+    warmup passes, then ``steps`` back-to-back passes (warm) and
+    ``min(steps, 20)`` passes each preceded by the read flush (flushed).
+    Inputs are freed before the next frame."""
     rep = {}
     for name in names:
         w = synthetic.WORKLOADS[name]
@@ -442,6 +444,8 @@ def time_workloads(zs, torch, dev, names, steps: int) -> dict:
         t = {k: torch.from_numpy(x[k]).to(dev) for k in ("dst", "coupling", "radial", "grad_out")}
         del x
         csr = zs.zs_build_csr(t["dst"], N)
+        ws = torch.empty(max(zs.zs_csr_workspace_bytes(E, N), 1), dtype=torch.uint8, device=dev)
+        flag = torch.zeros(1, dtype=torch.int32, device=dev)
         out = torch.empty((N, 16, C), device=dev)
         gc = torch.empty((E, 15), device=dev)
         gr = torch.empty((E, 3, C), device=dev)
@@ -449,6 +453,7 @@ def time_workloads(zs, torch, dev, names, steps: int) -> dict:
         nb = algorithmic_bytes(E, N, C)
 
         def pair(evs):
+            zs.zs_build_csr(t["dst"], N, workspace=ws, out=csr, bad_flag=flag)
             evs[0].record()
             zs.zs_forward(t["coupling"], t["radial"], csr, out=out)
             evs[1].record()
@@ -466,6 +471,8 @@ def time_workloads(zs, torch, dev, names, steps: int) -> dict:
                     flusher("read")
                 pair(e)
             torch.cuda.synchronize()
+            if int(flag.item()) != 0:
+                raise RuntimeError(f"destination index out of range in workload {name}")
             fwd = statistics.median(e[0].elapsed_time(e[1]) for e in evs) * 1e3
             bwd = statistics.median(e[1].elapsed_time(e[2]) for e in evs) * 1e3
             fb = statistics.median(e[0].elapsed_time(e[2]) for e in evs) * 1e3
@@ -478,12 +485,12 @@ def time_workloads(zs, torch, dev, names, steps: int) -> dict:
                      "target_us_at_60pct": round((nb["fwd"] + nb["bwd"]) /
                                                  (0.6 * PEAK_HBM_GBS * 1e9) * 1e6, 1),
                      **res}
-        del t, csr, out, gc, gr, flusher
+        del t, csr, ws, flag, out, gc, gr, flusher
         torch.cuda.empty_cache()
         progress(f"workload {name}: warm {res['warm']['fwd_bwd_us']} us, "
                  f"flushed {res['flushed']['fwd_bwd_us']} us")
-    rep["note"] = ("medians per call, forward and backward with an event between them; flushed: "
-                   + FLUSH_NOTES["read"])
+    rep["note"] = ("steps of CSR build, forward, backward; medians per call of the forward and "
+                   "the backward, with an event between them; flushed: " + FLUSH_NOTES["read"])
     return rep
 
 
