@@ -515,6 +515,39 @@ def test_strided_views(dev, label, N, E, C, slab, s0, band):
     check_grad_coupling(gc.cpu().numpy(), ref_gc, f"{label}: grad_coupling")
 
 
+@pytest.mark.parametrize("label,N,E,C", [("bcast_c32", 50, 3000, 32), ("bcast_c12", 17, 777, 12)])
+def test_broadcast_views(dev, label, N, E, C):
+    """Zero strides (the header allows them: inputs are only read): the
+    coupling and radial rows broadcast to every edge, and a radial view whose
+    three slots alias one row.  Results equal the oracle on materialised
+    copies of the same views."""
+    w = synthetic.custom(label, N, E, C, seed=6100 + E + C)
+    x = synthetic.make_inputs(w)
+    say(f"[gpu] broadcast views {label}: N={N} E={E} C={C}")
+    dst = torch.from_numpy(x["dst"]).to(dev)
+    csr = zs.zs_build_csr(dst, N)
+    g = torch.from_numpy(x["grad_out"]).to(dev)
+    row_c = torch.from_numpy(x["coupling"][:1].copy()).to(dev)          # (1, 15)
+    row_r = torch.from_numpy(x["radial"][:1].copy()).to(dev)            # (1, 3, C)
+    slot_r = torch.from_numpy(x["radial"][:, :1].copy()).to(dev)        # (E, 1, C)
+    cases = {
+        "both rows broadcast": (row_c.expand(E, 15), row_r.expand(E, 3, C)),
+        "radial slots aliased": (torch.from_numpy(x["coupling"]).to(dev), slot_r.expand(E, 3, C)),
+    }
+    for what, (cpl, rad) in cases.items():
+        assert cpl.stride(0) == 0 or rad.stride(1) == 0
+        out = zs.zs_forward(cpl, rad, csr)
+        gc, gr = zs.zs_backward(g, cpl, rad, csr)
+        torch.cuda.synchronize()
+        c_np = np.ascontiguousarray(cpl.cpu().numpy())
+        r_np = np.ascontiguousarray(rad.cpu().numpy())
+        ref_out = oracle.forward(c_np, r_np, x["dst"], N)
+        ref_gc, ref_gr = oracle.backward(x["grad_out"], c_np, r_np, x["dst"])
+        assert np.array_equal(_bits(out.cpu().numpy()), _bits(ref_out)), f"{label} {what}: forward"
+        assert np.array_equal(_bits(gr.cpu().numpy()), _bits(ref_gr)), f"{label} {what}: grad_radial"
+        check_grad_coupling(gc.cpu().numpy(), ref_gc, f"{label} {what}: grad_coupling")
+
+
 def test_hip_graph_capture_and_replay(dev):
     """The whole step (asynchronous CSR build, forward, backward; also the
     normalised pair) captured in one HIP graph and replayed several times, with
