@@ -514,24 +514,28 @@ constexpr uint32_t kBwdPartEdges = ZS_BWD_PART_EDGES;
 // several XCDs).
 constexpr int64_t kBwdPartShift = 8;
 
-// Start of part p of a node's len edges split into `parts` (p = parts: len):
-// floor(len * p / parts), for interior points rounded to the nearest multiple
-// of STEP (the edges one step of the wavefront takes), so that only a node's
-// last part ends with a partly filled step.  32-bit divisions by constants.
+// Start of part p of a node's len edges split into `parts` (p = parts: len),
+// in whole steps of STEP edges (the edges one step of the wavefront takes):
+// the node's ceil(len / STEP) steps are dealt so that the first (steps mod
+// parts) parts take one step more than the others.  Interior points are
+// multiples of STEP, so only the last part ends with a partly filled step,
+// and since parts are dispatched part-major, a node's shorter parts are the
+// ones that run last (a per-item timeline of the Poisson-degree frame showed
+// the kernel ending on late 6-step last parts).  32-bit divisions by constants.
 template <uint32_t STEP>
 __device__ __attribute__((always_inline)) inline uint32_t split_point(uint32_t len, uint32_t p,
                                                                       uint32_t parts) {
     if (p == 0) return 0;
     if (p >= parts) return len;
-    const uint64_t x = uint64_t(len) * p;
-    uint32_t at;
+    const uint32_t steps = (len + STEP - 1) / STEP;
+    uint32_t q, r;
     switch (parts) {
-        case 2: at = uint32_t(x / 2); break;
-        case 3: at = uint32_t(x / 3); break;
-        case 4: at = uint32_t(x / 4); break;
-        default: at = uint32_t(x / parts); break;
+        case 2: q = steps / 2; r = steps % 2; break;
+        case 3: q = steps / 3; r = steps % 3; break;
+        case 4: q = steps / 4; r = steps % 4; break;
+        default: q = steps / parts; r = steps % parts; break;
     }
-    at = (at + STEP / 2) / STEP * STEP;
+    const uint32_t at = (p * q + (p < r ? p : r)) * STEP;
     return at < len ? at : len;
 }
 
