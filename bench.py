@@ -36,6 +36,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -96,13 +97,24 @@ def algorithmic_bytes_normalized(n_edges: int, n_nodes: int, channels: int) -> d
             "bwd": b["bwd"] + N * (15 * C * 4 + 8) + 8 * E}
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without its comments, whitespace runs collapsed (so that
+    editing a comment does not invalidate counter data taken on the code)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(family: str | None = None) -> str:
-    """Hash of the sources (and build flags) of one kernel family, or of all."""
+    """Hash of the code (comments and whitespace ignored) of one kernel
+    family's sources, or of all, and of the build flags."""
     files = sorted({f for fam, fs in KERNEL_SOURCES.items() if family in (None, fam) for f in fs})
     h = hashlib.sha256()
-    for name in files + [os.path.join("..", "build.py")]:
-        with open(os.path.join(_CSRC, name), "rb") as f:
-            h.update(f.read())
+    for name in files:
+        with open(os.path.join(_CSRC, name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
+    with open(os.path.join(_CSRC, "..", "build.py"), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 

@@ -9,9 +9,9 @@
 //   grad_radial[e][l-1][c] = sum over rows r of degree l of g[r][c] * coupling[e][r-1]
 //   grad_coupling[e][r-1]  = sum over c of g[r][c] * radial[e][l(r)-1][c]
 //
-// Edges are visited grouped by destination (one workgroup per node, walking
-// the node's CSR range), so g[n] is read once per node into registers instead
-// of once per edge.  Within a wavefront, lane = b * NQ + q: b picks one of
+// Edges are visited grouped by destination (one wavefront per work item, a
+// node or a consecutive part of its CSR range), so g[n] is read once per work
+// item instead of once per edge.  Within a wavefront, lane = b * NQ + q: b picks one of
 // EPW = 64/NQ edges processed side by side, q picks VEC consecutive channels.
 // Each lane holds g[n][1..15] for its channels.
 //
@@ -202,8 +202,11 @@ __global__ __launch_bounds__(256) void zs_bwd_kernel(
 //    (3 x VEC per lane) and its coupling rows (EPW x 15 floats, fetched with
 //    coalesced all-distinct loads, at most two per lane) one step ahead into
 //    one of two register buffers, so loads overlap the previous step's math.
-//    Every load is unconditional (absent edges read a valid substitute) so the
-//    compiler can wait for exactly the buffer it consumes.
+//    Every load is unconditional (absent edges read a valid substitute), so
+//    within a step the compiler waits only for the buffer it consumes; at the
+//    head of the step loop it still waits for all loads, because address
+//    temporaries reuse registers the prefetch writes (measured harmless at four
+//    wavefronts per SIMD, where the other wavefronts keep the memory busy).
 //    The coupling floats go through LDS so every lane of an edge gets the
 //    edge's 15 weights.
 //  - The 15 row sums of grad_coupling are reduced in two rounds (rows 1-8 of
