@@ -92,6 +92,17 @@ def _counter_csv(path, counter, rows):
             wr.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
 
 
+def test_source_hash_ignores_comments_only():
+    """Counter data stays valid across comment and whitespace edits of a
+    kernel source, and not across any change of its code."""
+    src = "int f(int a) {  // adds one\n    return a + 1; /* the\n  sum */ }\n"
+    same = "// header\nint f(int a) {\n  return a + 1;\n}\n"
+    assert bench._code_only(src) == bench._code_only(same)
+    for changed in ("int f(int a) { return a + 2; }", "int f(int b) { return b + 1; }",
+                    "int f(int a) { return a - 1; }"):
+        assert bench._code_only(changed) != bench._code_only(src)
+
+
 def test_write_traffic_scales_by_the_copy(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
     kib = bench.COPY_CALIBRATION_BYTES / 1024
